@@ -1,0 +1,227 @@
+"""Benchmark of the fused exact-attention hot path on one MI355X.
+
+A step is one forward and one backward (every stage of the path: tiling,
+causal mask, online softmax, dropout, the O+LSE epilogue, the dO.O
+preprocess, recomputation and the dQ/dK/dV products) over the training
+workload B=4, H=32, N=4096, d=128, bf16, causal, dropout p=0.1, with the
+inputs resident in HBM.  The metric is attention TFLOP/s of forward +
+backward, counted as 3.5 * F with F = 4 B H N^2 d / 2 (causal), and its
+fraction of the bf16 dense matrix-core peak (2516.6 TFLOP/s).
+
+Prints one JSON line.  Besides the headline it reports the dominant
+kernel's roofline position (HIP-event timing of its launches over the timed
+region), the other stages' timings, secondary workloads, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, causal, d=128) + % of MFMA peak"
+KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "bwd_dkdv": "fa_bwd.hip", "bwd_dq": "fa_bwd.hip"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "io_aware_exact_20_amd", "csrc", name)
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "io_aware_exact_20_amd", "csrc", "fa_device.hpp")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def make_problem(fa, w, dev, with_bwd=True):
+    q, k, v, do = workloads.draw(w, with_dout=with_bwd)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    do = do.to(dev) if do is not None else None
+    return fa.Problem(q, k, v, do, scale=w.softmax_scale, causal=w.causal,
+                      dropout_p=w.dropout_p, seed=w.dropout_seed)
+
+
+def time_steps(prob, steps, warmup, with_bwd=True):
+    """Wall time per step plus per-stage HIP-event times (ms, per launch)."""
+    stages = [("fwd", prob.fwd)]
+    if with_bwd:
+        stages += [("bwd_prepare", prob.bwd_prepare), ("bwd_dkdv", prob.bwd_dkdv),
+                   ("bwd_dq", prob.bwd_dq)]
+    for _ in range(warmup):
+        for _, fn in stages:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    per = {}
+    for i, (name, _) in enumerate(stages):
+        per[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+    return wall, per
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec or rec.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle (forward + backward of whole heads of the same
+    workload) on the host cores for about `budget_s` seconds."""
+    import numpy as np
+    import oracle
+    q, k, v, do = workloads.draw(w)
+    f_head = w.flops_fwd() / (w.B * w.H) * 3.5
+    done, t_total = 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    p = float(np.float32(w.dropout_p))
+    while done < len(heads) and t_total < budget_s:
+        b, h = heads[done]
+        t0 = time.perf_counter()
+        oracle.bwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                   do[b:b + 1, h:h + 1], w.softmax_scale, w.causal, p, w.dropout_seed)
+        t_total += time.perf_counter() - t0
+        done += 1
+    # Note: the sliced heads are evaluated with (b, h) = (0, 0) dropout keys;
+    # the arithmetic per head is the same.
+    return {"value": f_head * done / t_total / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d heads (fwd+bwd, N=%d, d=%d, fp64), %.1f s" %
+                      (done, len(heads), w.N, w.d, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import io_aware_exact_20_amd as fa
+    fa.load()
+    dev = "cuda:0"
+    w = workloads.WORKLOADS["train_dropout"]
+    F = w.flops_fwd()
+    log("workload %s: B=%d H=%d N=%d d=%d causal p=%g" % (w.name, w.B, w.H, w.N, w.d, w.dropout_p))
+    prob = make_problem(fa, w, dev)
+    wall, per = time_steps(prob, args.steps, args.warmup)
+    value = 3.5 * F / (wall * 1e-3) / 1e12
+    log("step %.3f ms  -> %.1f TFLOP/s; stages %s" % (wall, value, per))
+
+    # Algorithmic flops credited to each kernel: the forward's two products;
+    # the backward's five (S recompute, dP, dV, dK, dQ) split as the dK/dV
+    # kernel's four and the dQ kernel's one -- its own S and dP recompute is
+    # extra work of this design and is not credited.
+    flops_per_launch = {"fwd": F, "bwd_dkdv": 2.0 * F, "bwd_dq": 0.5 * F}
+    dominant = max(flops_per_launch, key=lambda k: per[k])
+    bwd_ms = per["bwd_prepare"] + per["bwd_dkdv"] + per["bwd_dq"]
+    achieved = flops_per_launch[dominant] / (per[dominant] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(dominant),
+                "avg_launch_ms": round(per[dominant], 4)}
+
+    extras = {
+        "fwd_tflops": round(F / (per["fwd"] * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(2.5 * F / (bwd_ms * 1e-3) / 1e12, 2),
+        "stage_ms": {k: round(v, 4) for k, v in per.items()},
+    }
+    extras["fwd_pct_peak"] = round(100 * extras["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    extras["bwd_pct_peak"] = round(100 * extras["bwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    del prob
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        # Same shape without dropout (the dropout overhead), the long-context
+        # forward at N=4096, and the mid-size training shape.
+        w0 = workloads.Workload("train_nodropout", w.B, w.H, w.N, w.d, "bf16", causal=True,
+                                backward=True, seed=w.seed)
+        p0 = make_problem(fa, w0, dev)
+        wall0, per0 = time_steps(p0, max(5, args.steps // 2), 2)
+        extras["p0_fwd_tflops"] = round(F / (per0["fwd"] * 1e-3) / 1e12, 2)
+        extras["p0_bwd_tflops"] = round(2.5 * F / ((per0["bwd_prepare"] + per0["bwd_dkdv"]
+                                                    + per0["bwd_dq"]) * 1e-3) / 1e12, 2)
+        extras["p0_fwdbwd_tflops"] = round(3.5 * F / (wall0 * 1e-3) / 1e12, 2)
+        del p0
+        w4 = workloads.WORKLOADS["long_causal_4k"]
+        p4 = make_problem(fa, w4, dev, with_bwd=False)
+        _, per4 = time_steps(p4, max(10, args.steps), 3, with_bwd=False)
+        extras["long4k_fwd_tflops"] = round(w4.flops_fwd() / (per4["fwd"] * 1e-3) / 1e12, 2)
+        extras["long4k_fwd_pct_peak"] = round(100 * extras["long4k_fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+        del p4
+        w3 = workloads.WORKLOADS["mid_fwdbwd_causal"]
+        p3 = make_problem(fa, w3, dev)
+        wall3, _ = time_steps(p3, max(5, args.steps // 2), 2)
+        extras["mid_fwdbwd_tflops"] = round(3.5 * w3.flops_fwd() / (wall3 * 1e-3) / 1e12, 2)
+        del p3
+        torch.cuda.empty_cache()
+        log("extras %s" % extras)
+
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    if cpu:
+        log("cpu baseline %s" % cpu)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
+                   "dropout_p": w.dropout_p, "pass": "fwd+bwd",
+                   "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

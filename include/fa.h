@@ -1,0 +1,160 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention library.
+ *
+ * The library computes exact attention,
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * ("Vanilla Attention", displayed equation, mrodiduger.github.io page; the
+ * scale and mask are caller parameters), with the IO-aware method the pages
+ * describe: inputs are tiled into on-chip blocks, the softmax is formed
+ * online with a running row maximum and normaliser, and only O and one
+ * log-sum-exp per row are written back to HBM (interviewsvector.com page,
+ * "Architecture, step by step", steps 1-4; chipfoundryservices.com page,
+ * "FlashAttention Key Insight").  The backward recomputes the scores and
+ * probabilities from the stored statistics ("Recomputation",
+ * mrodiduger.github.io page) and returns dQ, dK and dV.  Masking and dropout
+ * are fused into both passes (same page, "Vanilla Attention" and
+ * "Experimental Results").
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are contiguous [B, H, N, d] in the element type `dtype`
+ *     (row-major, d fastest); lse and the backward's row statistics are
+ *     contiguous [B, H, N] float32 (natural logarithm).
+ *   - Every pointer argument is a DEVICE pointer, allocated and owned by the
+ *     caller; it must be 16-byte aligned.  Outputs must not alias inputs.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without synchronising.  The library never
+ *     allocates device memory; the backward's scratch is the caller's
+ *     `workspace`.
+ *   - Arguments are validated before any HIP call: FA_EINVAL for a bad value
+ *     or pointer, FA_EUNSUPPORTED for a well-formed request the library does
+ *     not implement.  FA_EHIP reports a failed launch; faults of enqueued work
+ *     surface at the caller's next synchronisation.  fa_last_error() returns
+ *     a message for the calling thread's last non-OK status.
+ *   - Calls are stateless and reentrant; concurrent calls on different
+ *     streams are independent.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_EINVAL = 1,        /* invalid argument (null/misaligned pointer, bad size or value) */
+    FA_EUNSUPPORTED = 2,  /* valid but not implemented (head dim, dtype) */
+    FA_EHIP = 3           /* a HIP launch or runtime call failed */
+} fa_status_t;
+
+typedef enum fa_dtype {
+    FA_F32 = 0,           /* float32 inputs, fp32 matrix-core products */
+    FA_BF16 = 1,          /* bfloat16 inputs, fp32 accumulation */
+    FA_F16 = 2            /* float16 inputs, fp32 accumulation */
+} fa_dtype_t;
+
+/*
+ * Problem description (64 bytes, no implicit padding).
+ *   B, H, N, d : batch, heads, sequence length, head dimension.  B, H, N >= 0
+ *                (a zero extent is an empty problem: FA_OK, nothing
+ *                launched); N < 2^31; d in {64, 128}.
+ *   dtype      : fa_dtype_t of q, k, v (and dout in the backward).
+ *   causal     : 0 or 1.  With 1, key j is masked for query i when j > i
+ *                (the diagonal is kept); masked probabilities are exactly 0.
+ *   scale      : finite and > 0; scores are scale * q.k (callers usually
+ *                pass 1/sqrt(d)).
+ *   dropout_p  : 0 <= p < 1.  Inverted dropout on the normalised
+ *                probabilities: kept entries are multiplied by
+ *                c = (float)(1/(1-p)); the row statistics are not affected.
+ *                The keep bit of (b, h, row, col) is lane (col & 7) of the
+ *                Philox-4x32-10 block (Salmon et al., SC'11) with counter
+ *                (col >> 3, row, h, b) and key (seed low 32, seed high 32);
+ *                lane 2w is the low and lane 2w+1 the high half of output
+ *                word w; kept iff lane >= round(p * 65536).
+ *   seed       : dropout seed (ignored when dropout_p == 0).
+ *   out_f32    : 0 -> outputs (o, dq, dk, dv) in `dtype`; 1 -> float32.
+ */
+typedef struct fa_params {
+    int64_t B, H, N, d;
+    int32_t dtype;
+    int32_t causal;
+    float scale;
+    float dropout_p;
+    uint64_t seed;
+    int32_t out_f32;
+    int32_t reserved;     /* must be 0 */
+} fa_params_t;
+
+/*
+ * Forward.  Reads q, k, v [B,H,N,d]; writes o [B,H,N,d] (dtype, or float32
+ * with out_f32) and lse [B,H,N] float32 with lse_i = ln sum_j exp(s_ij) over
+ * the visible keys of row i.  Nothing else is written to device memory.
+ */
+fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const void *v,
+                   void *o, float *lse, void *stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for `p` (0 for an empty problem,
+ * (size_t)-1 for invalid parameters): the fp32 row dot-products
+ * D_i = dO_i . O_i, [B,H,N], rounded up to 256 bytes.
+ */
+size_t fa_bwd_workspace_bytes(const fa_params_t *p);
+
+/*
+ * Backward.  Reads q, k, v and dout [B,H,N,d] in dtype, o (the forward's
+ * output, in the forward's output type: dtype, or float32 when out_f32)
+ * and lse (from fa_fwd); writes dq, dk, dv [B,H,N,d] (dtype, or float32
+ * with out_f32).  `workspace` must hold at least
+ * fa_bwd_workspace_bytes(p) bytes; its contents on entry are ignored.  The
+ * same p (scale, causal, dropout_p, seed) as the forward must be passed.
+ */
+fa_status_t fa_bwd(const fa_params_t *p, const void *q, const void *k, const void *v,
+                   const void *o, const float *lse, const void *dout,
+                   void *dq, void *dk, void *dv, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/*
+ * The backward as three stages, in the order fa_bwd enqueues them (all on
+ * one stream; later stages read the D_i the first one leaves in
+ * `workspace`):
+ *   fa_bwd_prepare  D_i = dO_i . O_i (fp32) into the workspace;
+ *   fa_bwd_dkdv     recomputes S and P tile by tile per key block and writes
+ *                   dK and dV;
+ *   fa_bwd_dq       recomputes S and P tile by tile per query block and
+ *                   writes dQ (no atomics: results are deterministic).
+ * Arguments mean the same as in fa_bwd; each stage validates its own.
+ */
+fa_status_t fa_bwd_prepare(const fa_params_t *p, const void *o, const void *dout,
+                           void *workspace, size_t workspace_bytes, void *stream);
+fa_status_t fa_bwd_dkdv(const fa_params_t *p, const void *q, const void *k, const void *v,
+                        const float *lse, const void *dout, void *dk, void *dv,
+                        const void *workspace, size_t workspace_bytes, void *stream);
+fa_status_t fa_bwd_dq(const fa_params_t *p, const void *q, const void *k, const void *v,
+                      const float *lse, const void *dout, void *dq, const void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
+ * Test hook: writes the dropout keep mask of plane (b, h) -- mask[row*N +
+ * col] = 1 when kept, 0 when dropped -- using the same device generator as
+ * the attention kernels.  Only B, H, N, dropout_p and seed of p are read
+ * (d and dtype are not checked).  mask is an N*N byte device buffer.
+ */
+fa_status_t fa_dropout_mask(const fa_params_t *p, int64_t b, int64_t h, uint8_t *mask,
+                            void *stream);
+
+/* Static description of a status code. */
+const char *fa_status_str(fa_status_t s);
+
+/* Message for the calling thread's most recent non-OK status ("" if none). */
+const char *fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,216 @@
+"""Python binding of the gfx950 fused exact-attention library (``libfa.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/fa.h``.  PyTorch supplies
+device memory and the current stream.  There is no fallback: if the
+library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["FAError", "Params", "Problem", "load", "fwd", "bwd", "bwd_workspace_bytes",
+           "dropout_mask", "F32", "BF16", "F16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
+F32, BF16, F16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+
+class FAError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("fa status %d: %s" % (status, message))
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    """Mirror of ``fa_params_t`` (64 bytes)."""
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dropout_p", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("out_f32", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(Params) == 64
+
+_lib = None
+
+
+def load():
+    """Load ``libfa.so`` once; raise if it is absent (build it with
+    ``python io_aware_exact_20_amd/build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfa.so not found at %s: build the HIP library first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, P, sz = ctypes.c_void_p, ctypes.POINTER(Params), ctypes.c_size_t
+    lib.fa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.argtypes = [P]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_prepare.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.fa_bwd_prepare.restype = ctypes.c_int
+    lib.fa_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fa_bwd_dkdv.restype = ctypes.c_int
+    lib.fa_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.fa_bwd_dq.restype = ctypes.c_int
+    lib.fa_dropout_mask.argtypes = [P, ctypes.c_int64, ctypes.c_int64, vp, vp]
+    lib.fa_dropout_mask.restype = ctypes.c_int
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FA_OK:
+        msg = _lib.fa_last_error().decode() or _lib.fa_status_str(status).decode()
+        raise FAError(status, msg)
+
+
+def make_params(B, H, N, d, dtype=BF16, scale=None, causal=False, dropout_p=0.0, seed=0,
+                out_f32=False) -> Params:
+    return Params(B=B, H=H, N=N, d=d, dtype=dtype,
+                  causal=int(bool(causal)),
+                  scale=float(scale if scale is not None else 1.0 / math.sqrt(d)),
+                  dropout_p=float(dropout_p), seed=int(seed) & (2**64 - 1),
+                  out_f32=int(bool(out_f32)), reserved=0)
+
+
+def _params_for(q: torch.Tensor, scale, causal, dropout_p, seed, out_f32) -> Params:
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError("unsupported dtype %s" % q.dtype)
+    B, H, N, d = q.shape
+    return make_params(B, H, N, d, _DTYPE_CODE[q.dtype], scale, causal, dropout_p, seed,
+                       out_f32)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, like, name):
+    if not t.is_cuda or not t.is_contiguous() or t.shape != like.shape:
+        raise ValueError("%s must be a contiguous device tensor of shape %s" %
+                         (name, tuple(like.shape)))
+
+
+def fwd(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out_f32=False):
+    """Fused forward: returns (o [B,H,N,d], lse [B,H,N] float32)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, q, n)
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share a dtype")
+    p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
+    o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                      _stream(q)))
+    return o, lse
+
+
+def bwd_workspace_bytes(q, scale=None, causal=False, dropout_p=0.0, seed=0, out_f32=False):
+    lib = load()
+    p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
+    n = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    if n == ctypes.c_size_t(-1).value:
+        raise FAError(FA_EINVAL, lib.fa_last_error().decode())
+    return n
+
+
+def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dropout_p=0.0, seed=0,
+        out_f32=False, workspace=None):
+    """Fused backward: returns (dq, dk, dv) with the forward's output type."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, q, n)
+    p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
+    out_dtype = torch.float32 if out_f32 else q.dtype
+    dq = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    dk = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    dv = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                      workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+class Problem:
+    """Preallocated outputs and workspace for repeated calls on one shape
+    (the benchmark's launch configuration).  Each method enqueues exactly
+    one library call on the current stream."""
+
+    def __init__(self, q, k, v, dout=None, scale=None, causal=False, dropout_p=0.0, seed=0,
+                 out_f32=False):
+        lib = load()
+        self.q, self.k, self.v, self.dout = q, k, v, dout
+        self.p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
+        odt = torch.float32 if out_f32 else q.dtype
+        self.o = torch.empty(q.shape, dtype=odt, device=q.device)
+        self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        if dout is not None:
+            self.dq = torch.empty(q.shape, dtype=odt, device=q.device)
+            self.dk = torch.empty(q.shape, dtype=odt, device=q.device)
+            self.dv = torch.empty(q.shape, dtype=odt, device=q.device)
+            n = lib.fa_bwd_workspace_bytes(ctypes.byref(self.p))
+            self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        self._s = _stream(q)
+
+    def fwd(self):
+        _check(_lib.fa_fwd(ctypes.byref(self.p), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                           _ptr(self.o), _ptr(self.lse), self._s))
+
+    def bwd_prepare(self):
+        _check(_lib.fa_bwd_prepare(ctypes.byref(self.p), _ptr(self.o), _ptr(self.dout),
+                                   _ptr(self.ws), self.ws.numel(), self._s))
+
+    def bwd_dkdv(self):
+        _check(_lib.fa_bwd_dkdv(ctypes.byref(self.p), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                                _ptr(self.lse), _ptr(self.dout), _ptr(self.dk), _ptr(self.dv),
+                                _ptr(self.ws), self.ws.numel(), self._s))
+
+    def bwd_dq(self):
+        _check(_lib.fa_bwd_dq(ctypes.byref(self.p), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                              _ptr(self.lse), _ptr(self.dout), _ptr(self.dq), _ptr(self.ws),
+                              self.ws.numel(), self._s))
+
+    def bwd(self):
+        self.bwd_prepare()
+        self.bwd_dkdv()
+        self.bwd_dq()
+
+
+def dropout_mask(B, H, N, dropout_p, seed, b, h, device="cuda"):
+    """Keep mask (uint8 [N, N], 1 = kept) of plane (b, h) from the device generator."""
+    lib = load()
+    p = make_params(B, H, N, 64, BF16, None, False, dropout_p, seed, False)
+    m = torch.empty((N, N), dtype=torch.uint8, device=device)
+    _check(lib.fa_dropout_mask(ctypes.byref(p), b, h, _ptr(m),
+                               ctypes.c_void_p(torch.cuda.current_stream(m.device).cuda_stream)))
+    return m

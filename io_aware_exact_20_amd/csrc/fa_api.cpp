@@ -1,0 +1,258 @@
+// C ABI of the attention library: argument validation, workspace sizing and
+// dispatch to the gfx950 kernels.  Validation happens before any HIP call,
+// so a rejected call never touches the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+fa_status_t fail(fa_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+fa_status_t fail(fa_status_t s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fa_status_t ok() {
+    g_last_error[0] = '\0';
+    return FA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+// Checks shared by every entry point.  *empty is set when there is nothing
+// to compute (a zero extent).
+fa_status_t check_params(const fa_params_t *p, bool *empty) {
+    if (!p) return fail(FA_EINVAL, "params is NULL");
+    if (p->B < 0 || p->H < 0 || p->N < 0)
+        return fail(FA_EINVAL, "negative extent B=%lld H=%lld N=%lld", (long long)p->B,
+                    (long long)p->H, (long long)p->N);
+    if (p->N > 0x7fffffffLL) return fail(FA_EINVAL, "N=%lld exceeds 2^31-1", (long long)p->N);
+    if (p->dtype != FA_F32 && p->dtype != FA_BF16 && p->dtype != FA_F16)
+        return fail(FA_EUNSUPPORTED, "dtype %d is not supported", (int)p->dtype);
+    if (p->d != 64 && p->d != 128)
+        return fail(FA_EUNSUPPORTED, "head dimension d=%lld is not supported (64 or 128)",
+                    (long long)p->d);
+    if (p->causal != 0 && p->causal != 1) return fail(FA_EINVAL, "causal must be 0 or 1");
+    if (!std::isfinite(p->scale) || !(p->scale > 0.f))
+        return fail(FA_EINVAL, "scale must be finite and positive (got %g)", (double)p->scale);
+    if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f))
+        return fail(FA_EINVAL, "dropout_p must be in [0, 1) (got %g)", (double)p->dropout_p);
+    if (p->out_f32 != 0 && p->out_f32 != 1) return fail(FA_EINVAL, "out_f32 must be 0 or 1");
+    if (p->reserved != 0) return fail(FA_EINVAL, "reserved field must be 0");
+    // B*H*N*d must be addressable; the product of the extents is bounded
+    // piecewise to avoid overflow in the check itself.
+    const double total = (double)p->B * (double)p->H * (double)p->N * (double)p->d;
+    if (total > 9.0e15) return fail(FA_EINVAL, "problem too large (B*H*N*d = %.3g)", total);
+    *empty = p->B == 0 || p->H == 0 || p->N == 0;
+    return FA_OK;
+}
+
+fa_status_t check_ptr(const void *ptr, const char *name) {
+    if (!ptr) return fail(FA_EINVAL, "%s is NULL", name);
+    if (!aligned16(ptr)) return fail(FA_EINVAL, "%s is not 16-byte aligned", name);
+    return FA_OK;
+}
+
+fa::Elem elem(int32_t dtype) {
+    return dtype == FA_F32 ? fa::Elem::F32 : dtype == FA_BF16 ? fa::Elem::BF16 : fa::Elem::F16;
+}
+
+uint32_t drop_threshold(float p) { return (uint32_t)std::llround((double)p * 65536.0); }
+float keep_scale(float p) { return (float)(1.0 / (1.0 - (double)p)); }
+
+size_t workspace_bytes(const fa_params_t *p) {
+    // The fp32 row dot-products D_i, padded to 256 bytes.
+    const size_t rows = (size_t)p->B * (size_t)p->H * (size_t)p->N;
+    return (rows * 4 + 255) / 256 * 256;
+}
+
+fa_status_t hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(FA_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const void *v, void *o,
+                   float *lse, void *stream) {
+    bool empty = false;
+    fa_status_t s = check_params(p, &empty);
+    if (s != FA_OK) return s;
+    if (empty) return ok();
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")))
+        return s;
+    fa::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = p->B; a.H = p->H; a.N = p->N;
+    a.scale_log2 = p->scale * 1.44269504088896340736f;
+    const bool dropout = p->dropout_p > 0.f;
+    a.drop_T = dropout ? drop_threshold(p->dropout_p) : 0;
+    a.drop_c = dropout ? keep_scale(p->dropout_p) : 1.f;
+    a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
+    a.seed_hi = (uint32_t)(p->seed >> 32);
+    a.out_f32 = p->out_f32;
+    return hip_status(fa::launch_fwd(elem(p->dtype), (int)p->d, p->causal != 0, dropout, a,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                      "fa_fwd launch");
+}
+
+size_t fa_bwd_workspace_bytes(const fa_params_t *p) {
+    bool empty = false;
+    if (check_params(p, &empty) != FA_OK) return (size_t)-1;
+    if (empty) return 0;
+    return workspace_bytes(p);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Common part of the backward entry points: parameter and workspace checks,
+// and the argument block (the workspace holds D).
+fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t workspace_size,
+                      bool *empty, fa::BwdArgs *a) {
+    fa_status_t s = check_params(p, empty);
+    if (s != FA_OK || *empty) return s;
+    if ((s = check_ptr(workspace, "workspace"))) return s;
+    const size_t need = workspace_bytes(p);
+    if (workspace_size < need)
+        return fail(FA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_size, need);
+    *a = fa::BwdArgs{};
+    a->dvec = reinterpret_cast<float *>(const_cast<void *>(workspace));
+    a->B = p->B; a->H = p->H; a->N = p->N;
+    a->scale = p->scale;
+    a->scale_log2 = p->scale * 1.44269504088896340736f;
+    const bool dropout = p->dropout_p > 0.f;
+    a->drop_T = dropout ? drop_threshold(p->dropout_p) : 0;
+    a->drop_c = dropout ? keep_scale(p->dropout_p) : 1.f;
+    a->seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
+    a->seed_hi = (uint32_t)(p->seed >> 32);
+    a->out_f32 = p->out_f32;
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_bwd_prepare(const fa_params_t *p, const void *o, const void *dout,
+                           void *workspace, size_t workspace_size, void *stream) {
+    bool empty = false;
+    fa::BwdArgs a;
+    fa_status_t s = bwd_setup(p, workspace, workspace_size, &empty, &a);
+    if (s != FA_OK) return s;
+    if (empty) return ok();
+    if ((s = check_ptr(o, "o")) || (s = check_ptr(dout, "dout"))) return s;
+    a.o = o; a.dout = dout;
+    return hip_status(fa::launch_bwd_pre(elem(p->dtype), (int)p->d, a,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                      "fa_bwd_prepare launch");
+}
+
+fa_status_t fa_bwd_dkdv(const fa_params_t *p, const void *q, const void *k, const void *v,
+                        const float *lse, const void *dout, void *dk, void *dv,
+                        const void *workspace, size_t workspace_size, void *stream) {
+    bool empty = false;
+    fa::BwdArgs a;
+    fa_status_t s = bwd_setup(p, workspace, workspace_size, &empty, &a);
+    if (s != FA_OK) return s;
+    if (empty) return ok();
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(lse, "lse")) || (s = check_ptr(dout, "dout")) ||
+        (s = check_ptr(dk, "dk")) || (s = check_ptr(dv, "dv")))
+        return s;
+    a.q = q; a.k = k; a.v = v; a.lse = lse; a.dout = dout; a.dk = dk; a.dv = dv;
+    return hip_status(fa::launch_bwd_dkdv(elem(p->dtype), (int)p->d, p->causal != 0,
+                                          p->dropout_p > 0.f, a,
+                                          reinterpret_cast<hipStream_t>(stream)),
+                      "fa_bwd_dkdv launch");
+}
+
+fa_status_t fa_bwd_dq(const fa_params_t *p, const void *q, const void *k, const void *v,
+                      const float *lse, const void *dout, void *dq, const void *workspace,
+                      size_t workspace_size, void *stream) {
+    bool empty = false;
+    fa::BwdArgs a;
+    fa_status_t s = bwd_setup(p, workspace, workspace_size, &empty, &a);
+    if (s != FA_OK) return s;
+    if (empty) return ok();
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(lse, "lse")) || (s = check_ptr(dout, "dout")) || (s = check_ptr(dq, "dq")))
+        return s;
+    a.q = q; a.k = k; a.v = v; a.lse = lse; a.dout = dout; a.dq = dq;
+    return hip_status(fa::launch_bwd_dq(elem(p->dtype), (int)p->d, p->causal != 0,
+                                        p->dropout_p > 0.f, a,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                      "fa_bwd_dq launch");
+}
+
+fa_status_t fa_bwd(const fa_params_t *p, const void *q, const void *k, const void *v,
+                   const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                   void *dv, void *workspace, size_t workspace_size, void *stream) {
+    bool empty = false;
+    fa::BwdArgs a;
+    fa_status_t s = bwd_setup(p, workspace, workspace_size, &empty, &a);
+    if (s != FA_OK) return s;
+    if (empty) return ok();
+    // Every pointer is checked before the first stage is enqueued.
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")) || (s = check_ptr(dout, "dout")) ||
+        (s = check_ptr(dq, "dq")) || (s = check_ptr(dk, "dk")) || (s = check_ptr(dv, "dv")))
+        return s;
+    if ((s = fa_bwd_prepare(p, o, dout, workspace, workspace_size, stream))) return s;
+    if ((s = fa_bwd_dkdv(p, q, k, v, lse, dout, dk, dv, workspace, workspace_size, stream)))
+        return s;
+    return fa_bwd_dq(p, q, k, v, lse, dout, dq, workspace, workspace_size, stream);
+}
+
+fa_status_t fa_dropout_mask(const fa_params_t *p, int64_t b, int64_t h, uint8_t *mask,
+                            void *stream) {
+    if (!p) return fail(FA_EINVAL, "params is NULL");
+    if (p->B < 0 || p->H < 0 || p->N < 0) return fail(FA_EINVAL, "negative extent");
+    if (p->N > 0x7fffffffLL) return fail(FA_EINVAL, "N exceeds 2^31-1");
+    if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f))
+        return fail(FA_EINVAL, "dropout_p must be in [0, 1)");
+    if (b < 0 || b >= p->B || h < 0 || h >= p->H)
+        return fail(FA_EINVAL, "plane (b=%lld, h=%lld) outside B=%lld H=%lld", (long long)b,
+                    (long long)h, (long long)p->B, (long long)p->H);
+    if (p->N == 0) return ok();
+    if (!mask) return fail(FA_EINVAL, "mask is NULL");
+    const uint32_t T = p->dropout_p > 0.f ? drop_threshold(p->dropout_p) : 0;
+    return hip_status(fa::launch_dropout_mask(p->N, T, (uint32_t)(p->seed & 0xFFFFFFFFu),
+                                              (uint32_t)(p->seed >> 32), b, h, mask,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      "fa_dropout_mask launch");
+}
+
+const char *fa_status_str(fa_status_t s) {
+    switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_EINVAL: return "FA_EINVAL: invalid argument";
+    case FA_EUNSUPPORTED: return "FA_EUNSUPPORTED: unsupported configuration";
+    case FA_EHIP: return "FA_EHIP: HIP runtime error";
+    }
+    return "unknown fa_status_t";
+}
+
+const char *fa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

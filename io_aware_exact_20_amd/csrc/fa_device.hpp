@@ -1,0 +1,297 @@
+// Device-side building blocks of the gfx950 attention kernels: element
+// types, matrix-core fragments, wavefront exchanges and the dropout
+// generator.  Everything here is written for CDNA4 (64-lane wavefronts,
+// 32x32 MFMA tiles).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- fragments
+//
+// A fragment is one lane's share of a 32x16 operand of a 32x32 MFMA tile:
+// eight elements along the contraction dimension.  For 16-bit types it is
+// one register quadruple feeding a single v_mfma_f32_32x32x16 instruction;
+// for fp32 it is eight registers feeding eight v_mfma_f32_32x32x2f32.  The
+// A and B operands of one product always fill their eight slots with the
+// same contraction indices, so the hardware's own slot order cancels out.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; typedef bf16x4 half; };
+template <> struct Frag<f16> { typedef f16x8 type; typedef f16x4 half; };
+template <> struct Frag<float> { typedef f32x8 type; typedef f32x4 half; };
+
+template <typename T> using frag_t = typename Frag<T>::type;
+template <typename T> using half_t = typename Frag<T>::half;
+
+// acc += A(32x16) * B(16x32) on the matrix cores.
+__device__ __forceinline__ void mma(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16 &acc, const f16x8 &a, const f16x8 &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16 &acc, const f32x8 &a, const f32x8 &b) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+}
+
+// Round-to-nearest-even conversions from fp32.
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ f16 from_f32<f16>(float x) { return (f16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+
+// Join two half-fragments (four contraction indices each) into a fragment.
+template <typename T>
+__device__ __forceinline__ frag_t<T> join(const half_t<T> &lo, const half_t<T> &hi) {
+    frag_t<T> f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f[i] = lo[i]; f[i + 4] = hi[i]; }
+    return f;
+}
+
+// Eight fp32 values rounded into a fragment.
+template <typename T>
+__device__ __forceinline__ frag_t<T> pack8(const float *x) {
+    frag_t<T> f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = from_f32<T>(x[i]);
+    return f;
+}
+
+// Eight consecutive accumulator registers (from `off`) rounded into a fragment.
+template <typename T>
+__device__ __forceinline__ frag_t<T> pack8(const f32x16 &x, int off) {
+    frag_t<T> f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = from_f32<T>(x[off + i]);
+    return f;
+}
+
+// ------------------------------------------------------------ lane exchange
+//
+// Exchanges between the two halves of a wavefront (lane ^ 32) go through
+// ds_bpermute.  (v_permlane32_swap would avoid the LDS crossbar, but when fed
+// the same value for both operands this compiler treats its two results as
+// equal and drops the partner's value, so it is not used.)
+
+__device__ __forceinline__ uint32_t lane_in_wave() { return threadIdx.x & (kWave - 1); }
+
+// Value held by lane ^ 32.
+__device__ __forceinline__ uint32_t other_half(uint32_t x) {
+    return (uint32_t)__shfl_xor((int)x, 32);
+}
+
+// max(x, x of lane ^ 32), identical in both lanes.
+__device__ __forceinline__ float max_halves(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+// x + (x of lane ^ 32), bitwise identical in both lanes.
+__device__ __forceinline__ float sum_halves(float x) {
+    const float y = __shfl_xor(x, 32);
+    return (lane_in_wave() & 32) ? y + x : x + y;
+}
+
+// ------------------------------------------------------------------ dropout
+//
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, SC'11): a keyed
+// bijection on four 32-bit words built from two 32x32->64-bit products per
+// round, with the key advanced by two Weyl increments between rounds.
+struct Philox4 { uint32_t x[4]; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+    constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t hiA = __umulhi(kMulA, c0), loA = kMulA * c0;
+        const uint32_t hiB = __umulhi(kMulB, c2), loB = kMulB * c2;
+        const uint32_t n0 = hiB ^ c1 ^ k0;
+        const uint32_t n2 = hiA ^ c3 ^ k1;
+        c0 = n0; c1 = loB; c2 = n2; c3 = loA;
+        k0 += kWeylA; k1 += kWeylB;
+    }
+    Philox4 out;
+    out.x[0] = c0; out.x[1] = c1; out.x[2] = c2; out.x[3] = c3;
+    return out;
+}
+
+// Keep bits of the eight columns 8*grp .. 8*grp+7 of one row: bit e is set
+// when column 8*grp+e survives (its 16-bit lane >= threshold).
+__device__ __forceinline__ uint32_t keep_byte(uint32_t grp, uint32_t row, uint32_t h, uint32_t b,
+                                              uint32_t seed_lo, uint32_t seed_hi,
+                                              uint32_t threshold) {
+    const Philox4 r = philox4x32_10(grp, row, h, b, seed_lo, seed_hi);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        bits |= (uint32_t)((r.x[w] & 0xFFFFu) >= threshold) << (2 * w);
+        bits |= (uint32_t)((r.x[w] >> 16) >= threshold) << (2 * w + 1);
+    }
+    return bits;
+}
+
+// Keep bits of the sixteen keys one lane holds in a 32x32 accumulator that
+// has one query row per lane (register r <-> key kbase + 8(r/4) + 4g +
+// r%4, g = lane / 32): bit r of the result.  Each half-wavefront draws two
+// of the row's four 8-key Philox blocks (keys kbase + 16g .. + 15) and the
+// halves exchange the nibbles the other one needs.
+__device__ __forceinline__ uint32_t keep_bits_row(uint32_t kbase, uint32_t row, uint32_t h,
+                                                  uint32_t b, uint32_t seed_lo, uint32_t seed_hi,
+                                                  uint32_t threshold) {
+    const uint32_t g = lane_in_wave() >> 5;
+    const uint32_t grp = (kbase >> 3) + 2 * g;
+    const uint32_t bits = keep_byte(grp, row, h, b, seed_lo, seed_hi, threshold) |
+                          (keep_byte(grp + 1, row, h, b, seed_lo, seed_hi, threshold) << 8);
+    const uint32_t mine = g ? 4 : 0, theirs = g ? 0 : 4;
+    const uint32_t own = ((bits >> mine) & 0xFu) | (((bits >> (8 + mine)) & 0xFu) << 4);
+    const uint32_t send = ((bits >> theirs) & 0xFu) | (((bits >> (8 + theirs)) & 0xFu) << 4);
+    const uint32_t recv = other_half(send);
+    return g ? (recv | (own << 8)) : (own | (recv << 8));
+}
+
+// ------------------------------------------------------------ memory moves
+//
+// Eight (a fragment) or four (a half-fragment) consecutive elements moved
+// with 16-byte (or 8-byte) vector accesses.  Addresses are multiples of the
+// access size.
+template <typename T>
+__device__ __forceinline__ frag_t<T> load_frag(const T *p) {
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_bit_cast(frag_t<T>, *reinterpret_cast<const uint4 *>(p));
+    } else {
+        struct Two { uint4 a, b; } t;
+        t.a = reinterpret_cast<const uint4 *>(p)[0];
+        t.b = reinterpret_cast<const uint4 *>(p)[1];
+        return __builtin_bit_cast(frag_t<T>, t);
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ half_t<T> load_half(const T *p) {
+    if constexpr (sizeof(T) == 2) {
+        return __builtin_bit_cast(half_t<T>, *reinterpret_cast<const uint2 *>(p));
+    } else {
+        return __builtin_bit_cast(half_t<T>, *reinterpret_cast<const uint4 *>(p));
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_half(T *p, const half_t<T> &x) {
+    if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, x);
+    } else {
+        *reinterpret_cast<uint4 *>(p) = __builtin_bit_cast(uint4, x);
+    }
+}
+
+// Four fp32 values rounded to T and stored as one vector.
+template <typename T>
+__device__ __forceinline__ void store4(T *p, float a, float b, float c, float d) {
+    half_t<T> x;
+    x[0] = from_f32<T>(a); x[1] = from_f32<T>(b); x[2] = from_f32<T>(c); x[3] = from_f32<T>(d);
+    store_half<T>(p, x);
+}
+
+// ---------------------------------------------------------- transposed reads
+//
+// Half-fragment of a transposed operand read from a row-major LDS tile:
+// lane l (i = l % 32, g = l / 32) receives tile[rbase + 4g + k][c0 + i] for
+// k = 0..3.  Two such reads (rbase and rbase + 8) give the eight slots of a
+// fragment whose contraction index runs along the tile's rows in the order
+// rbase + 4g + {0..3}, rbase + 8 + 4g + {0..3} -- the order in which a
+// 32x32 accumulator holds the same rows (register r -> row 8(r/4) + 4g +
+// r%4), so a rounded accumulator is the matching other operand.
+//
+// For 16-bit types this is one ds_read_b64_tr_b16: within each group of 16
+// lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
+// 4k + i/4 (k = 0..3), so lane 4k + j of group G addresses row
+// rbase + 4(G/2) + k at column c0 + 16(G%2) + 4j.  fp32 tiles are read
+// element by element.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ half_t<T> load_half_tr(const T *tile, int ld, int rbase, int c0) {
+    const int lane = (int)lane_in_wave();
+    if constexpr (sizeof(T) == 2) {
+        const int G = lane >> 4, k = (lane >> 2) & 3, j = lane & 3;
+        const T *p = tile + (rbase + 4 * (G >> 1) + k) * ld + c0 + 16 * (G & 1) + 4 * j;
+        const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(p));
+        return __builtin_bit_cast(half_t<T>, r);
+    } else {
+        const int i = lane & 31, g = lane >> 5;
+        half_t<T> h;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[k] = tile[(rbase + 4 * g + k) * ld + c0 + i];
+        return h;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ frag_t<T> load_frag_tr(const T *tile, int ld, int rbase, int c0) {
+    return join<T>(load_half_tr<T>(tile, ld, rbase, c0), load_half_tr<T>(tile, ld, rbase + 8, c0));
+}
+
+// ------------------------------------------------------------- tile copies
+//
+// Cooperative copy of ROWS consecutive rows (from row r0) of a row-major
+// [N, D] matrix into a row-major LDS tile of pitch LD, staged through
+// registers so that the global loads of the next tile can be in flight
+// while the current one is consumed.  Rows at or past N read as zero.
+template <typename T, int ROWS, int D, int THREADS>
+struct TileCopy {
+    static constexpr int CH = 16 / sizeof(T);          // elements per 16-byte chunk
+    static constexpr int CPR = D / CH;                 // chunks per row
+    static constexpr int CHUNKS = ROWS * CPR;
+    static constexpr int PER = (CHUNKS + THREADS - 1) / THREADS;
+    uint4 r[PER];
+
+    __device__ __forceinline__ void load(const T *g, int64_t r0, int64_t N, int tid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + i * THREADS;
+            const int row = c / CPR, col = (c % CPR) * CH;
+            r[i] = uint4{0, 0, 0, 0};
+            if ((CHUNKS % THREADS == 0 || c < CHUNKS) && r0 + row < N)
+                r[i] = *reinterpret_cast<const uint4 *>(g + (r0 + row) * D + col);
+        }
+    }
+
+    template <int LD>
+    __device__ __forceinline__ void store(T *lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + i * THREADS;
+            if (CHUNKS % THREADS == 0 || c < CHUNKS) {
+                const int row = c / CPR, col = (c % CPR) * CH;
+                *reinterpret_cast<uint4 *>(lds + row * LD + col) = r[i];
+            }
+        }
+    }
+};
+
+// --------------------------------------------------------------- utilities
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T> __device__ __forceinline__ T zero_el() { return from_f32<T>(0.f); }
+
+}  // namespace fa

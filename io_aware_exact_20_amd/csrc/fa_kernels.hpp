@@ -1,0 +1,50 @@
+// Kernel argument blocks and host-side launchers shared between the C ABI
+// layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum class Elem { F32 = 0, BF16 = 1, F16 = 2 };
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int64_t B, H, N;
+    float scale_log2;     // softmax scale times log2(e)
+    float drop_c;         // keep scale 1/(1-p) rounded to float
+    uint32_t drop_T;      // 16-bit drop threshold round(p * 65536)
+    uint32_t seed_lo, seed_hi;
+    int32_t out_f32;
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    float *dvec;          // workspace: D_i = dO_i . O_i, [B,H,N]
+    int64_t B, H, N;
+    float scale;          // softmax scale
+    float scale_log2;     // scale * log2(e)
+    float drop_c;
+    uint32_t drop_T;
+    uint32_t seed_lo, seed_hi;
+    int32_t out_f32;      // o, dout and the gradients are fp32 when set
+};
+
+// Each launcher enqueues its kernels on `stream` and returns the status of
+// the launch (hipSuccess when enqueued).
+hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
+                      hipStream_t stream);
+hipError_t launch_bwd_pre(Elem e, int d, const BwdArgs &a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
+                           hipStream_t stream);
+hipError_t launch_bwd_dq(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
+                         hipStream_t stream);
+hipError_t launch_dropout_mask(int64_t N, uint32_t T, uint32_t seed_lo, uint32_t seed_hi,
+                               int64_t b, int64_t h, uint8_t *mask, hipStream_t stream);
+
+}  // namespace fa

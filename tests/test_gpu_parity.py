@@ -1,0 +1,347 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (per tensor): fp32 inputs max-abs <= 1e-5; bf16 / fp16 inputs
+max-abs <= 2e-2 and mean-abs <= 2e-3.  Integer-valued outcomes (dropout
+masks, causal and tile zero patterns) must match exactly.
+
+Storage rounding.  A bf16 output carries up to half an ulp of rounding on
+top of the computation (0.0156 for |x| in [4, 8)), so the 2e-2 max-abs bar
+is applied to the computed values themselves: strictly to the run whose
+outputs are written in fp32 (``out_f32=1``, same kernels), and to the
+16-bit-output run with half an output ulp of |exact| added per element.
+The mean-abs bar applies unchanged to the 16-bit-output run.
+
+The oracle gets the exact float64 up-cast of the same rounded inputs and the
+dropout probability rounded to float32, as the library receives it.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, None), "bf16": (2e-2, 2e-3), "f16": (2e-2, 2e-3)}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def p32(p):
+    return float(np.float32(p))
+
+
+MANTISSA_BITS = {torch.bfloat16: 7, torch.float16: 10, torch.float32: 23}
+
+
+def half_ulp(x, torch_dtype):
+    """Half a unit in the last place of |x| in the given storage type."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - MANTISSA_BITS[torch_dtype] - 1), 0.0)
+
+
+def compare(name, got, exact, dtype):
+    """Max/mean abs error of `got` (torch, any device) against `exact` (f64).
+
+    16-bit outputs get half an output ulp of |exact| on top of the max-abs
+    bar (the storage rounding); fp32 outputs are held to the bar itself."""
+    g = got.detach().double().cpu().numpy()
+    e = np.asarray(exact)
+    assert np.isfinite(g).all(), "%s has non-finite values" % name
+    err = np.abs(g - e)
+    tmax, tmean = TOL[dtype]
+    slack = half_ulp(e, got.dtype) if got.dtype != torch.float32 else 0.0
+    excess = err - slack
+    mx, mn = float(err.max(initial=0.0)), float(err.mean()) if err.size else 0.0
+    mx_ex = float(excess.max(initial=0.0))
+    log("  %-4s max|err| %.3e (less storage %.3e) mean|err| %.3e max|x| %.2f [%s]" %
+        (name, mx, mx_ex, mn, float(np.abs(e).max(initial=0)), str(got.dtype)[6:]))
+    assert mx_ex <= tmax, "%s max-abs error %.3e (beyond storage rounding) > %.1e" % (
+        name, mx_ex, tmax)
+    if tmean is not None:
+        assert mn <= tmean, "%s mean-abs error %.3e > %.1e" % (name, mn, tmean)
+
+
+def run_fwd(fa, w: Workload, q, k, v, out_f32=False):
+    dev = "cuda"
+    o, lse = fa.fwd(q.to(dev), k.to(dev), v.to(dev), scale=w.softmax_scale, causal=w.causal,
+                    dropout_p=w.dropout_p, seed=w.dropout_seed, out_f32=out_f32)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def run_bwd(fa, w: Workload, q, k, v, do, out_f32=False):
+    dev = "cuda"
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = fa.fwd(qd, kd, vd, scale=w.softmax_scale, causal=w.causal, dropout_p=w.dropout_p,
+                    seed=w.dropout_seed, out_f32=out_f32)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, scale=w.softmax_scale, causal=w.causal,
+                        dropout_p=w.dropout_p, seed=w.dropout_seed, out_f32=out_f32)
+    torch.cuda.synchronize()
+    return o, lse, dq, dk, dv
+
+
+def oracle_fwd(w, q, k, v, heads=None):
+    return oracle.fwd(q, k, v, w.softmax_scale, w.causal, p32(w.dropout_p), w.dropout_seed,
+                      heads=heads)
+
+
+def oracle_bwd(w, q, k, v, do, heads=None):
+    return oracle.bwd(q, k, v, do, w.softmax_scale, w.causal, p32(w.dropout_p), w.dropout_seed,
+                      heads=heads)
+
+
+# ------------------------------------------------------- full comparisons
+
+SMALL = []
+for dt in ("bf16", "f16", "f32"):
+    for d in (64, 128):
+        for causal in (False, True):
+            for p in (0.0, 0.1):
+                SMALL.append(Workload("small_%s_d%d_c%d_p%g" % (dt, d, causal, p), 2, 3, 300, d,
+                                      dt, causal=causal, dropout_p=p, backward=True,
+                                      seed=11 + d + 3 * causal, dropout_seed=0xC0FFEE + d))
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_fwd_bwd_full(gpu_lib, w):
+    """Every element of O, LSE, dQ, dK, dV at N=300 (several tiles plus a
+    ragged tail), both head dims, masks, dropout and all input types."""
+    log("case %s" % w.name)
+    q, k, v, do = workloads.draw(w)
+    edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
+    for out_f32 in ((False, True) if w.dtype != "f32" else (False,)):
+        o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do, out_f32=out_f32)
+        for name, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
+                                 ("dK", dk, edk), ("dV", dv, edv)):
+            compare(name, got, exact, w.dtype)
+
+
+def test_single_head_f32_fwd_bwd(gpu_lib):
+    """B=1,H=1,N=128,d=64 fp32 non-causal forward and backward: max-abs 1e-5."""
+    w = workloads.WORKLOADS["single_head_f32"]
+    log("case %s" % w.name)
+    q, k, v, do = workloads.draw(w)
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
+    edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
+    for name, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
+                             ("dK", dk, edk), ("dV", dv, edv)):
+        compare(name, got, exact, "f32")
+
+
+@pytest.mark.parametrize("name", ["small_fwd_bf16", "small_fwd_bf16_causal"])
+def test_small_forward_all_heads(gpu_lib, name):
+    """B=2,H=8,N=1024,d=64 bf16 forward, non-causal and causal, every head."""
+    w = workloads.WORKLOADS[name]
+    log("case %s" % w.name)
+    q, k, v, _ = workloads.draw(w)
+    o, lse = run_fwd(gpu_lib, w, q, k, v)
+    eo, elx = oracle_fwd(w, q, k, v)
+    compare("O", o, eo, w.dtype)
+    compare("LSE", lse, elx, w.dtype)
+
+
+# --------------------------------------------- full-size, sampled heads
+
+@pytest.mark.parametrize("name,heads", [
+    ("mid_fwdbwd_causal", [(0, 0), (3, 7), (7, 15)]),
+    ("train_dropout", [(0, 0), (1, 13), (3, 31)]),
+])
+def test_full_size_fwd_bwd_sampled_heads(gpu_lib, name, heads):
+    """The full workloads in the benchmark's launch configuration; every
+    element of the sampled (b, h) heads is compared."""
+    w = workloads.WORKLOADS[name]
+    log("case %s heads %s" % (w.name, heads))
+    q, k, v, do = workloads.draw(w)
+    edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do, heads=heads)
+    for out_f32 in (False, True):
+        o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do, out_f32=out_f32)
+        for b, h in heads:
+            log(" head (%d, %d) out_f32=%d" % (b, h, out_f32))
+            for nm, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
+                                   ("dK", dk, edk), ("dV", dv, edv)):
+                compare(nm, got[b, h], exact[b, h], w.dtype)
+        del o, lse, dq, dk, dv
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["long_causal_4k", "long_causal_16k"])
+def test_long_context_forward_sampled_heads(gpu_lib, name):
+    w = workloads.WORKLOADS[name]
+    heads = [(0, 0), (0, 31)] if w.N <= 4096 else [(0, 13)]
+    log("case %s heads %s" % (w.name, heads))
+    q, k, v, _ = workloads.draw(w)
+    o, lse = run_fwd(gpu_lib, w, q, k, v)
+    eo, elx = oracle_fwd(w, q, k, v, heads=heads)
+    for b, h in heads:
+        compare("O", o[b, h], eo[b, h], w.dtype)
+        compare("LSE", lse[b, h], elx[b, h], w.dtype)
+
+
+def test_long_context_65536_sampled_rows(gpu_lib):
+    """N=65536: rows are independent in the forward, so a seeded sample of
+    rows (the first, tile-boundary rows at stride 4096, the last, random) of
+    two heads is compared."""
+    w = workloads.WORKLOADS["long_causal_64k"]
+    log("case %s" % w.name)
+    q, k, v, _ = workloads.draw(w)
+    free0 = torch.cuda.mem_get_info()[0]
+    o, lse = run_fwd(gpu_lib, w, q, k, v)
+    N = w.N
+    rng = np.random.default_rng(65536)
+    rows = set(range(0, 64)) | set(range(N - 32, N))
+    for t in range(4096, N, 4096):
+        rows |= {t - 1, t, t + 1}
+    rows |= set(int(x) for x in rng.integers(0, N, size=96))
+    rows = sorted(rows)
+    for b, h in [(0, 13), (0, 31)]:
+        eo, elx = oracle.fwd_rows(q, k, v, b, h, rows, w.softmax_scale, w.causal)
+        compare("O", o[b, h, rows], eo, w.dtype)
+        compare("LSE", lse[b, h, rows], elx, w.dtype)
+    del free0
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("N", [1, 2, 63, 65, 127, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(gpu_lib, N, causal):
+    w = Workload("ragged", 1, 2, N, 128, "bf16", causal=causal, dropout_p=0.2, backward=True,
+                 seed=N, dropout_seed=N * 31 + 7)
+    q, k, v, do = workloads.draw(w)
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
+    edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
+    for name, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
+                             ("dK", dk, edk), ("dV", dv, edv)):
+        compare(name, got, exact, w.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_key_returns_value_exactly(gpu_lib, dtype):
+    """N = 1: exp(0) = 1 and l = 1, so O must equal V bit for bit and
+    LSE = scale q.k; dV = dO bit for bit and dQ = dK = 0 (to rounding)."""
+    w = Workload("n1", 3, 4, 1, 64, dtype, causal=True, backward=True, seed=99)
+    q, k, v, do = workloads.draw(w)
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
+    assert torch.equal(o.cpu(), v)
+    assert torch.equal(dv.cpu(), do)
+    # dS = P (dP - D) is zero only up to fp32 rounding of dO.V against dO.O.
+    assert float(dq.abs().max()) <= 1e-5 and float(dk.abs().max()) <= 1e-5
+    ref = w.softmax_scale * (q.double() * k.double()).sum(-1)
+    assert float((lse.cpu().double() - ref).abs().max()) < 1e-5
+
+
+def test_zero_query_gives_prefix_mean(gpu_lib):
+    w = Workload("q0", 1, 2, 333, 128, "bf16", causal=True, seed=5)
+    _, k, v, _ = workloads.draw(w)
+    q = torch.zeros_like(k)
+    o, lse = run_fwd(gpu_lib, w, q, k, v)
+    vv = v.double().numpy()
+    counts = np.arange(1, w.N + 1)
+    expect = np.cumsum(vv, axis=2) / counts[None, None, :, None]
+    compare("O", o, expect, "bf16")
+    compare("LSE", lse, np.broadcast_to(np.log(counts), lse.shape), "bf16")
+
+
+def test_empty_problem(gpu_lib):
+    q = torch.empty((2, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = gpu_lib.fwd(q, q, q)
+    assert o.shape == q.shape and lse.shape == (2, 2, 0)
+    dq, dk, dv = gpu_lib.bwd(q, q, q, o, lse, q)
+    assert dq.shape == q.shape
+
+
+def test_out_f32_matches_oracle(gpu_lib):
+    w = Workload("outf32", 1, 2, 200, 128, "bf16", causal=True, dropout_p=0.1, backward=True,
+                 seed=21, dropout_seed=4)
+    q, k, v, do = workloads.draw(w)
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do, out_f32=True)
+    assert o.dtype == torch.float32 and dq.dtype == torch.float32
+    edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
+    for name, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
+                             ("dK", dk, edk), ("dV", dv, edv)):
+        compare(name, got, exact, "bf16")
+
+
+def test_forward_is_deterministic(gpu_lib):
+    w = workloads.WORKLOADS["train_dropout"]
+    w = Workload("det", 2, 4, 1024, 128, "bf16", causal=True, dropout_p=0.1, seed=3,
+                 dropout_seed=w.dropout_seed)
+    q, k, v, _ = workloads.draw(w)
+    o1, l1 = run_fwd(gpu_lib, w, q, k, v)
+    o2, l2 = run_fwd(gpu_lib, w, q, k, v)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------ bit-exact probes
+
+def test_dropout_mask_bit_exact_full_planes(gpu_lib):
+    """The device generator reproduces the oracle's keep mask bit for bit on
+    whole (b, h) planes of the training workload."""
+    w = workloads.WORKLOADS["train_dropout"]
+    for b, h in [(0, 0), (3, 31), (2, 17)]:
+        got = gpu_lib.dropout_mask(w.B, w.H, w.N, w.dropout_p, w.dropout_seed, b, h).cpu().numpy()
+        exact = oracle.dropout_mask(w.N, p32(w.dropout_p), w.dropout_seed, b, h)
+        log("  plane (%d,%d) kept %.5f mismatches %d" % (b, h, got.mean(), int((got != exact).sum())))
+        assert np.array_equal(got, exact)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("p", [0.0, 0.3])
+def test_identity_values_expose_zero_pattern(gpu_lib, d, p):
+    """N = d and V = I: O[i, j] = P~[i, j], which must be exactly zero iff
+    key j is masked (j > i) or dropped."""
+    N = d
+    w = Workload("ident", 2, 2, N, d, "bf16", causal=True, dropout_p=p, seed=d,
+                 dropout_seed=1234 + d)
+    q, k, _, _ = workloads.draw(w)
+    v = torch.eye(N, dtype=torch.bfloat16).expand(2, 2, N, N).contiguous()
+    o, _ = run_fwd(gpu_lib, w, q, k, v)
+    for b in range(2):
+        for h in range(2):
+            keep = oracle.dropout_mask(N, p32(p), w.dropout_seed, b, h).astype(bool)
+            visible = np.tril(np.ones((N, N), dtype=bool)) & keep
+            got = o[b, h].float().cpu().numpy() != 0.0
+            assert np.array_equal(got, visible)
+
+
+def test_tile_boundary_probe_at_full_shape(gpu_lib):
+    """Training shape: V has one-hot columns on 128 keys at tile boundaries,
+    so O[:, c] = P~[:, probe_c] and its zero pattern must equal the oracle's
+    keep & causal pattern exactly; dO one-hot on the probe rows exposes rows
+    of P~ through dV."""
+    w = workloads.WORKLOADS["train_dropout"]
+    B, H, N, d = 1, 2, w.N, w.d
+    w = Workload("probe", B, H, N, d, "bf16", causal=True, dropout_p=w.dropout_p,
+                 backward=True, seed=17, dropout_seed=w.dropout_seed)
+    q, k, _, _ = workloads.draw(w)
+    probes = []
+    for t in np.linspace(1, N // 32 - 1, 43).astype(int) * 32:
+        probes += [int(t) - 1, int(t), int(t) + 1]
+    probes = sorted(set(x for x in probes if 0 <= x < N))[:d]
+    assert len(probes) == d
+    v = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    do = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    for c, j in enumerate(probes):
+        v[:, :, j, c] = 1.0
+        do[:, :, j, c] = 1.0
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
+    rows = np.arange(N)
+    for h in range(H):
+        keep = oracle.dropout_mask(N, p32(w.dropout_p), w.dropout_seed, 0, h).astype(bool)
+        for c, j in enumerate(probes):
+            col_expect = keep[:, j] & (rows >= j)      # P~[:, j] != 0
+            col_got = o[0, h, :, c].float().cpu().numpy() != 0
+            assert np.array_equal(col_got, col_expect), (h, c, j)
+            row_expect = keep[j, :] & (rows <= j)      # P~[j, :] != 0
+            row_got = dv[0, h, :, c].float().cpu().numpy() != 0
+            assert np.array_equal(row_got, row_expect), (h, c, j)
