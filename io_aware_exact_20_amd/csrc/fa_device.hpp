@@ -121,8 +121,11 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t hiA = __umulhi(kMulA, c0), loA = kMulA * c0;
-        const uint32_t hiB = __umulhi(kMulB, c2), loB = kMulB * c2;
+        // One 32x32->64-bit product per word pair (v_mad_u64_u32 gives both
+        // halves in a single instruction).
+        const uint64_t pA = (uint64_t)kMulA * c0, pB = (uint64_t)kMulB * c2;
+        const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
+        const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
         const uint32_t n0 = hiB ^ c1 ^ k0;
         const uint32_t n2 = hiA ^ c3 ^ k1;
         c0 = n0; c1 = loB; c2 = n2; c3 = loA;
@@ -287,6 +290,67 @@ struct TileCopy {
         }
     }
 };
+
+// ------------------------------------------------------ swizzled LDS tiles
+//
+// A tile of 16-bit elements with D columns is stored with a row pitch of
+// exactly 2D bytes; the 16-byte chunks of row r are permuted, logical chunk
+// x sitting at position x ^ f(r).  On gfx950 the LDS serves a 16-byte read
+// for 16 lanes (or an 8-byte read for 32 lanes) per cycle across 64 banks of
+// 4 bytes.  f is chosen so that both access patterns of the attention
+// kernels are free of bank conflicts: 16 lanes reading the same logical
+// chunk of 16 consecutive rows (matrix-core operands taken along a row), and
+// 32 lanes reading 64 contiguous bytes of 4 consecutive rows (transposed
+// reads).  An unpadded pitch also lets whole rows be filled by direct
+// global-to-LDS loads, which write 16 bytes per lane contiguously.
+#define FA_LDS __attribute__((address_space(3)))
+
+template <int D>
+struct Swz {
+    static constexpr int CPR = D / 8;            // 16-byte chunks per row
+    static constexpr int ROW_BYTES = D * 2;
+    __device__ static constexpr uint32_t f(uint32_t r) {
+        return D == 128 ? (((r & 3u) << 2) | ((r >> 2) & 3u))
+                        : ((((r >> 1) & 1u) << 2) | ((r >> 2) & 3u));
+    }
+    // Byte offset of element column `col` (a multiple of 4) of row r.
+    __device__ static constexpr uint32_t off(uint32_t r, uint32_t col) {
+        return r * ROW_BYTES + ((((col >> 3) ^ f(r))) << 4) + (col & 7u) * 2;
+    }
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte LDS read at byte address `addr` (the compiler folds constant
+// parts into the instruction's offset field).
+template <typename T>
+__device__ __forceinline__ frag_t<T> lds_frag(uint32_t addr) {
+    return __builtin_bit_cast(frag_t<T>, *(const FA_LDS u32x4 *)(uintptr_t)addr);
+}
+
+// Transposed half-fragment read (ds_read_b64_tr_b16) at byte address addr.
+template <typename T>
+__device__ __forceinline__ half_t<T> lds_half_tr(uint32_t addr) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(uintptr_t)addr);
+    return __builtin_bit_cast(half_t<T>, r);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's data
+// lands at lds_base + 16 l (lds_base must be uniform across the wavefront).
+__device__ __forceinline__ void g2lds16(const void *gptr, uint32_t lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void *)(uintptr_t)lds_base, 16, 0, 0);
+}
+
+// Register-class hint: the value is placed in accumulation registers (AGPRs)
+// at this point.  The statement emits no instruction; matrix-core
+// instructions read their operands and accumulators from AGPRs directly,
+// which keeps long-lived operands (the query block, the output
+// accumulators) out of the VGPRs that the softmax arithmetic needs.
+template <typename V>
+__device__ __forceinline__ void pin_agpr(V &x) { asm volatile("" : "+a"(x)); }
+// Same for the vector registers (values the VALU works on).
+template <typename V>
+__device__ __forceinline__ void pin_vgpr(V &x) { asm volatile("" : "+v"(x)); }
 
 // --------------------------------------------------------------- utilities
 
