@@ -320,25 +320,42 @@ struct Swz {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef FA_LDS char lds_char;
 
-// 16-byte LDS read at byte address `addr` (the compiler folds constant
-// parts into the instruction's offset field).
+// 16-byte LDS read (the compiler folds constant parts of the address into
+// the instruction's offset field).  LDS tiles are addressed through
+// pointers derived from distinct __shared__ arrays, so that the compiler
+// can tell a direct global-to-LDS load into one buffer from a read of
+// another and need not wait for the load before the read.
 template <typename T>
-__device__ __forceinline__ frag_t<T> lds_frag(uint32_t addr) {
-    return __builtin_bit_cast(frag_t<T>, *(const FA_LDS u32x4 *)(uintptr_t)addr);
+__device__ __forceinline__ frag_t<T> lds_frag(const lds_char *p) {
+    return __builtin_bit_cast(frag_t<T>, *(const FA_LDS u32x4 *)p);
 }
 
-// Transposed half-fragment read (ds_read_b64_tr_b16) at byte address addr.
+// Transposed half-fragment read (ds_read_b64_tr_b16).
 template <typename T>
-__device__ __forceinline__ half_t<T> lds_half_tr(uint32_t addr) {
-    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)(uintptr_t)addr);
+__device__ __forceinline__ half_t<T> lds_half_tr(const lds_char *p) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)p);
     return __builtin_bit_cast(half_t<T>, r);
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's data
-// lands at lds_base + 16 l (lds_base must be uniform across the wavefront).
-__device__ __forceinline__ void g2lds16(const void *gptr, uint32_t lds_base) {
-    __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void *)(uintptr_t)lds_base, 16, 0, 0);
+// lands at base + 16 l (base must be uniform across the wavefront).
+__device__ __forceinline__ void g2lds16(const void *gptr, lds_char *base) {
+    __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void *)base, 16, 0, 0);
+}
+
+// Buffer resource over `bytes` bytes from `p` (raw, unswizzled).  Loads
+// through it whose 16 bytes lie past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane at byte offset voff + soff of the buffer straight into
+// LDS at base + 16 l; lanes past the buffer end write zeros.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          lds_char *base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void *)base, 16, voff, soff, 0, 0);
 }
 
 // Register-class hint: the value is placed in accumulation registers (AGPRs)

@@ -249,7 +249,7 @@ struct Fwd16Tile {
     static constexpr int RW = 64;                 // query rows per wavefront
     static constexpr int NB = RW / 32;            // 32-row blocks per wavefront
     static constexpr int BQ = NW * RW;            // query rows per workgroup
-    static constexpr int BC = 64;                 // keys per tile
+    static constexpr int BC = 32;                 // keys per tile
     static constexpr int THREADS = NW * kWave;
     static constexpr int TILE_BYTES = BC * D * 2;
     static constexpr int LOADS = TILE_BYTES / (kWave * 16) / NW;   // per wave per tile
@@ -291,14 +291,13 @@ __global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a)
     constexpr int NB = TL::NB, BQ = TL::BQ, BC = TL::BC, RW = TL::RW;
     constexpr int TB = TL::TILE_BYTES, LOADS = TL::LOADS;
     constexpr int RB = SW::ROW_BYTES;
-    constexpr int NDC = D / 16;   // contraction chunks of S
+    constexpr int NDC = D / 16;   // contraction chunks of S (K fragments per tile)
     constexpr int NDB = D / 32;   // 32-column blocks of O
-    constexpr int NKB = BC / 32;  // 32-key blocks of a tile
     constexpr float kNegInf = -__builtin_huge_valf();
+    static_assert(BC == 32 && NB == 2, "the step schedule below assumes 32-key tiles, 2 row blocks");
 
     // LDS: K buffers at [0, 2TB), V buffers at [2TB, 4TB).
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(FA_LDS char *)smem;
+    __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], vs0[TB], vs1[TB];
 
     const int lane = (int)lane_in_wave();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -345,44 +344,63 @@ __global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a)
             for (int db = 0; db < NDB; ++db)
                 voff[hf][db] = SW::off(8 * hf + 4 * (G >> 1) + k, 32 * db + 16 * (G & 1) + 4 * j);
     }
-    // ---- per-lane global offsets (elements) of the direct tile loads.
-    uint32_t grow[LOADS], gcol[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int L = (i * NW + wave) * kWave + lane;     // 16-byte chunk of the tile
-        const int R = L / SW::CPR, pos = L % SW::CPR;
-        grow[i] = (uint32_t)R;
-        gcol[i] = (uint32_t)((pos ^ (int)SW::f(R)) * 8);
-    }
+    // ---- direct tile loads: wave-instruction i of this wave fills tile rows
+    // R0 + i * RSTEP (R0 = first row of instruction 0 for this lane); the
+    // swizzled column of a lane does not depend on i.  Loads go through
+    // buffer resources bounded by the head's end, so the rows of the last
+    // tile past N arrive as zeros (masked scores, zero values).
+    constexpr int RSTEP = NW * kWave / SW::CPR;
+    const int R0 = (wave * kWave + lane) / SW::CPR;
+    const uint32_t gcol = (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0)) * 8);
+    static_assert(RSTEP % 16 == 0, "the swizzle must repeat every RSTEP rows");
+    const uint32_t lane_boff = ((uint32_t)R0 * D + gcol) * 2;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
 
     const int kend = CAUSAL ? (q0 + BQ < N ? q0 + BQ : N) : N;
-    const int ntiles = (kend + BC - 1) / BC;
+    const int NT = (kend + BC - 1) / BC;                 // tiles the workgroup streams
     // Tiles this wavefront needs (causal: up to its own last row).
     const int wend = CAUSAL ? (q0w + RW < N ? q0w + RW : N) : N;
-    const int wtiles = (wend + BC - 1) / BC;
+    const int Tw = (wend + BC - 1) / BC;
 
-    auto load_tile = [&](int t, int buf) {
+    // Load i of this wave's share of tile t of K (or V) into a buffer.
+    auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf_lds, int i) {
+        buf2lds16(rs, lane_boff, (uint32_t)((t * BC + i * RSTEP) * D * 2),
+                  buf_lds + (wave + i * NW) * (kWave * 16));
+    };
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf_lds) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) load_part(rs, t, buf_lds, i);
+    };
+    auto kbuf = [&](int buf) { return buf ? (lds_char *)ks1 : (lds_char *)ks0; };
+    auto vbuf = [&](int buf) { return buf ? (lds_char *)vs1 : (lds_char *)vs0; };
+
+    // A tile needs masking if it reaches past the sequence end or, causal,
+    // past this wavefront's first query row.
+    auto is_edge = [&](int t) { return (t * BC + BC > N) || (CAUSAL && t * BC + BC - 1 > q0w); };
+    // Scores of tile t set to -inf where the key is masked for the query.
+    auto apply_mask = [&](f32x16 (&s)[NB], int t) {
         const int k0 = t * BC;
-        const uint32_t kb_lds = lds0 + buf * TB + wave * (kWave * 16);
-        const uint32_t vb_lds = lds0 + 2 * TB + buf * TB + wave * (kWave * 16);
-        if (k0 + BC <= N) {
-            const T *Kt = K + (size_t)k0 * D, *Vt = V + (size_t)k0 * D;
+        // Register r of block nb holds key k0 + 4g + kk(r) for query
+        // q0w + 32nb + lq, kk(r) = 8(r/4) + r%4.  Masked: key >= N, or
+        // (causal) key > query, i.e. kk(r) > lim[nb].
+        int lim[NB];
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const uint32_t e = grow[i] * D + gcol[i];
-                g2lds16(Kt + e, kb_lds + i * NW * (kWave * 16));
-                g2lds16(Vt + e, vb_lds + i * NW * (kWave * 16));
+        for (int nb = 0; nb < NB; ++nb) {
+            int l = N - 1 - (k0 + 4 * g);
+            if (CAUSAL) {
+                const int c = q0w + 32 * nb + lq - (k0 + 4 * g);
+                l = c < l ? c : l;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                int r = k0 + (int)grow[i];
-                r = r < N ? r : N - 1;
-                const size_t e = (size_t)r * D + gcol[i];
-                g2lds16(K + e, kb_lds + i * NW * (kWave * 16));
-                g2lds16(V + e, vb_lds + i * NW * (kWave * 16));
-            }
+            lim[nb] = l;
         }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r / 4) + (r % 4);
+                if (kk > lim[nb]) s[nb][r] = kNegInf;
+            }
     };
 
     const float sl2 = a.scale_log2;
@@ -393,159 +411,235 @@ __global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a)
         m_run[nb] = kNegInf;
         l_run[nb] = 0.f;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            o[db][nb] = f32x16{};
-            pin_agpr(o[db][nb]);
-        }
+        for (int db = 0; db < NDB; ++db) o[db][nb] = f32x16{};
     }
 
-    // One key tile: K in buffer BUF of the K area, V in buffer BUF of the V
-    // area (BUF is a compile-time constant so that every LDS address is a
-    // per-lane register plus an immediate).
-    auto tile = [&](auto buf_c, int t) {
-        constexpr int BUF = decltype(buf_c)::value;
-        constexpr uint32_t KB = BUF * TB, VB = 2 * TB + BUF * TB;
-        const int k0 = t * BC;
-
-        // ---- S^T = K Q^T: s[kb][nb] register r <-> key k0 + 32kb + 8(r/4) + 4g + r%4,
-        // query q0w + 32nb + lq.
-        f32x16 s[NKB][NB];
+    // ---- building blocks.
+    // Keep bits of tile t: keep[nb] bit r <-> register r of score block nb.
+    auto draw_keep = [&](uint32_t (&keep)[NB], int t) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s[kb][nb] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < NDC; ++c) {
-                const frag_t<T> kf = lds_frag<T>(lds0 + KB + kb * 32 * RB + koff[c]);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) mma(s[kb][nb], kf, qf[nb][c]);
-            }
-        }
-
-        // ---- causal and sequence-end masks (edge tiles only).
-        const bool edge = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0w);
-        if (edge) {
-            const int rel = k0 + 4 * g - (q0w + lq);   // key - query at kb = nb = r = 0
-            const int kmax = N - 1 - (k0 + 4 * g);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int kk = 32 * kb + 8 * (r / 4) + (r % 4);
-                        const bool masked = (kk > kmax) || (CAUSAL && rel + kk - 32 * nb > 0);
-                        if (masked) s[kb][nb][r] = kNegInf;
-                    }
-        }
-
-        // ---- row maxima of the tile (this lane's half of the keys).
-        float mx[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            float x = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(s[kb][nb][r], s[kb][nb][r + 1]));
-            mx[nb] = x;
-        }
+        for (int nb = 0; nb < NB; ++nb)
+            keep[nb] = keep_bits_row((uint32_t)(t * BC), (uint32_t)(q0w + 32 * nb + lq), h_idx, b_idx,
+                                     a.seed_lo, a.seed_hi, a.drop_T);
+    };
+    // Move the reference maxima when a tile exceeds them by the threshold.
+    auto maybe_rescale = [&](const float (&mx)[NB]) {
         bool need = false;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) need |= mx[nb] * sl2 > m_run[nb] + kRescaleLog2;
         if (__builtin_expect(__ballot(need) != 0, 0)) {
-            // Move the reference maxima to the exact row maxima.
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const float m_new = fmaxf(m_run[nb], max_halves(mx[nb]) * sl2);
                 const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run[nb] - m_new);
                 l_run[nb] *= alpha;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    pin_agpr(o[db][nb]);
-                    o[db][nb] *= alpha;
-                    pin_agpr(o[db][nb]);
-                }
+                for (int db = 0; db < NDB; ++db) o[db][nb] *= alpha;
                 m_run[nb] = m_new;
             }
         }
-
-        // ---- probabilities against the reference maxima; row sums of the
-        // rounded values; dropout; O^T += V^T P^T.
-        uint32_t pp[NKB][NB][8];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const float mu = m_run[nb] == kNegInf ? 0.f : m_run[nb];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p0 = fast_exp2(fmaf(s[kb][nb][2 * i], sl2, -mu));
-                    const float p1 = fast_exp2(fmaf(s[kb][nb][2 * i + 1], sl2, -mu));
-                    pp[kb][nb][i] = pack2<T>(p0, p1);
-                }
-            float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    acc0 = sum2<T>(pp[kb][nb][i], acc0);
-                    acc1 = sum2<T>(pp[kb][nb][i + 1], acc1);
-                }
-            l_run[nb] += acc0 + acc1;
-        }
-        if (DROPOUT) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const uint32_t keep = keep_bits_row((uint32_t)(k0 + 32 * kb),
-                                                        (uint32_t)(q0w + 32 * nb + lq), h_idx,
-                                                        b_idx, a.seed_lo, a.seed_hi, a.drop_T);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint32_t m0 = ((keep >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u;
-                        const uint32_t m1 = ((keep >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u;
-                        pp[kb][nb][i] &= (m0 | m1);
-                    }
-                }
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const uint32_t kc_off = (uint32_t)((32 * kb + 16 * cc) * RB);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const frag_t<T> vf = join<T>(lds_half_tr<T>(lds0 + VB + kc_off + voff[0][db]),
-                                                 lds_half_tr<T>(lds0 + VB + kc_off + voff[1][db]));
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        u32x4 pv;
-                        pv[0] = pp[kb][nb][4 * cc + 0];
-                        pv[1] = pp[kb][nb][4 * cc + 1];
-                        pv[2] = pp[kb][nb][4 * cc + 2];
-                        pv[3] = pp[kb][nb][4 * cc + 3];
-                        mma(o[db][nb], vf, __builtin_bit_cast(frag_t<T>, pv));
-                    }
-                }
-            }
     };
 
-    // Tile loop, two tiles per trip (buffers 0 and 1).  Tile t+1 is fetched
-    // while tile t is consumed; one barrier per tile frees the buffer the
-    // next fetch overwrites.
-    load_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0): this wave's tile loads have landed
+    // One pipelined step for tile t (scores sc, maxima mx).  Matrix-core
+    // work: S of tile t+1 (NDC K fragments x 2 products, from K buffer
+    // (t+1)&1) and O^T += V^T P^T of tile t (2 NDB V fragments x 2 products,
+    // V buffer t&1).  The VALU work -- tile t's 16 probability pairs and row
+    // sums, tile t+1's maxima -- is spread over the products so that no gap
+    // between two products holds more than about four VALU instructions (a
+    // single wavefront co-issues that many with a 32x32x16 product; more
+    // stall the matrix core).  The next tiles' loads are spread over the
+    // same groups.  LDS fragments are read two groups ahead of their use.
+    //   B (S of t+1):  pairs 0..11 (key chunk 0 complete, chunk 1 half);
+    //   C (PV of t):   pairs 12..15 in the first half (before chunk 1's
+    //                  products), row sums and the maxima of tile t+1.
+    constexpr int SB = NDC;                  // K fragment groups (2 products each)
+    constexpr int SC = 2 * NDB;              // V fragment groups (2 products each)
+    static_assert(SB == 8 || SB == 4, "group plan for d = 128 or 64");
+    constexpr int PB = 12;                   // pairs computed in B
+    uint32_t keep_cur[NB];
+    auto step = [&](auto par_c, auto hn_c, f32x16 (&sc)[NB], f32x16 (&sn)[NB], float (&mx)[NB], int t) {
+        constexpr int VB = decltype(par_c)::value, KN = VB ^ 1;
+        constexpr bool HN = decltype(hn_c)::value;
+        const lds_char *kbl = KN ? (lds_char *)ks1 : (lds_char *)ks0;
+        const lds_char *vbl = VB ? (lds_char *)vs1 : (lds_char *)vs0;
+
+        maybe_rescale(mx);
+        float mu[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mu[nb] = m_run[nb] == kNegInf ? 0.f : m_run[nb];
+        if (HN) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sn[nb] = f32x16{};
+        }
+
+        auto kfrag = [&](int j) { return lds_frag<T>(kbl + koff[j]); };
+        auto vfrag = [&](int j) {
+            const int cc = j / NDB, db = j % NDB;
+            const uint32_t kc_off = (uint32_t)(16 * cc * RB);
+            return join<T>(lds_half_tr<T>(vbl + kc_off + voff[0][db]),
+                           lds_half_tr<T>(vbl + kc_off + voff[1][db]));
+        };
+        uint32_t pp[NB][8];
+        auto pfrag = [&](int nb, int cc) {
+            u32x4 pv;
+            pv[0] = pp[nb][4 * cc + 0];
+            pv[1] = pp[nb][4 * cc + 1];
+            pv[2] = pp[nb][4 * cc + 2];
+            pv[3] = pp[nb][4 * cc + 3];
+            return __builtin_bit_cast(frag_t<T>, pv);
+        };
+        float acc[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) { acc[nb][0] = 0.f; acc[nb][1] = 0.f; }
+        // Pair p = (row block p & 1, registers 2i, 2i+1 with i = p >> 1).
+        auto pair = [&](int p) {
+            const int nb = p & 1, i = p >> 1;
+            const float p0 = fast_exp2(fmaf(sc[nb][2 * i], sl2, -mu[nb]));
+            const float p1 = fast_exp2(fmaf(sc[nb][2 * i + 1], sl2, -mu[nb]));
+            pp[nb][i] = pack2<T>(p0, p1);
+            if (DROPOUT) {
+                // The row sums keep the dropped probabilities.
+                acc[nb][i & 1] = sum2<T>(pp[nb][i], acc[nb][i & 1]);
+                const uint32_t m0 = ((keep_cur[nb] >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u;
+                const uint32_t m1 = ((keep_cur[nb] >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u;
+                pp[nb][i] &= (m0 | m1);
+            }
+            pin_vgpr(pp[nb][i]);   // keeps the work in its group (no sinking)
+        };
+        auto rowsum = [&](int w) {   // w = pair index
+            if (!DROPOUT) {
+                const int nb = w & 1, i = w >> 1;
+                acc[nb][i & 1] = sum2<T>(pp[nb][i], acc[nb][i & 1]);
+            }
+        };
+        float mxp[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) mxp[nb] = kNegInf;
+        auto maxpair = [&](int w) {   // registers 2w, 2w+1 (of 16) of both row blocks
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                mxp[nb] = fmaxf(mxp[nb], fmaxf(sn[nb][2 * w], sn[nb][2 * w + 1]));
+        };
+
+        // ---- B: S of tile t+1 | pairs 0..11 | K loads of tile t+2.
+        frag_t<T> kf[3], vf[3];
+        if (HN) { kf[0] = kfrag(0); kf[1] = kfrag(1); }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+            if (HN) {
+                if (j + 2 < SB) kf[(j + 2) % 3] = kfrag(j + 2);
+                mma(sn[0], kf[j % 3], qf[0][j]);
+            }
+            // Pairs of this group: PB pairs spread over SB groups in order.
+#pragma unroll
+            for (int p = (j * PB) / SB; p < ((j + 1) * PB) / SB; ++p) pair(p);
+            if (HN) mma(sn[1], kf[j % 3], qf[1][j]);
+            if (j < LOADS) load_part(krs, t + 2, kbuf(VB), j);
+            if (j == SB - 2) vf[0] = vfrag(0);
+            if (j == SB - 1) vf[1] = vfrag(1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (HN && is_edge(t + 1)) apply_mask(sn, t + 1);
+
+        // ---- C: PV of tile t | pairs 12..15, row sums, maxima of t+1 | V loads of t+1.
+        constexpr int HALF = SC / 2;             // groups that use key chunk 0
+#pragma unroll
+        for (int j = 0; j < SC; ++j) {
+            if (j + 2 < SC) vf[(j + 2) % 3] = vfrag(j + 2);
+            const int cc = j / NDB, db = j % NDB;
+            mma(o[db][0], vf[j % 3], pfrag(0, cc));
+            if (j < HALF) {
+                // pairs 12..15 (chunk 1), sums 0..3
+#pragma unroll
+                for (int p = PB + (j * 4) / HALF; p < PB + ((j + 1) * 4) / HALF; ++p) pair(p);
+#pragma unroll
+                for (int w = (j * 4) / HALF; w < ((j + 1) * 4) / HALF; ++w) rowsum(w);
+            } else {
+                // sums 4..15
+                const int jj = j - HALF;
+#pragma unroll
+                for (int w = 4 + (jj * 12) / HALF; w < 4 + ((jj + 1) * 12) / HALF; ++w) rowsum(w);
+            }
+            if (HN) {
+#pragma unroll
+                for (int w = (j * 8) / SC; w < ((j + 1) * 8) / SC; ++w) maxpair(w);
+            }
+            mma(o[db][1], vf[j % 3], pfrag(1, cc));
+            if (j < LOADS) load_part(vrs, t + 1, vbuf(KN), j);
+            if (j == SC - 1) {
+                // Keep the row sums and maxima in this group (no sinking).
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    pin_vgpr(acc[nb][0]);
+                    pin_vgpr(acc[nb][1]);
+                    if (HN) pin_vgpr(mxp[nb]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) l_run[nb] += acc[nb][0] + acc[nb][1];
+        if (HN) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) mx[nb] = mxp[nb];
+            if (DROPOUT) draw_keep(keep_cur, t + 1);
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of K_{t+2}, V_{t+1} landed
+        __syncthreads();                 // ... everyone's; buffers of K_{t+1}, V_t free
+    };
+
+    // ---- prologue: K_0, K_1, V_0; S and maxima of tile 0.
+    f32x16 sA[NB], sB[NB];
+    float mx[NB];
+    load_tile(krs, 0, kbuf(0));
+    load_tile(krs, 1, kbuf(1));
+    load_tile(vrs, 0, vbuf(0));
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < ntiles; t += 2) {
-        if (t + 1 < ntiles) load_tile(t + 1, 1);
-        if (t < wtiles) tile(std::integral_constant<int, 0>{}, t);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (t + 1 >= ntiles) break;
-        if (t + 2 < ntiles) load_tile(t + 2, 0);
-        if (t + 1 < wtiles) tile(std::integral_constant<int, 1>{}, t + 1);
+    if (Tw > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sA[nb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+            const frag_t<T> kf = lds_frag<T>(kbuf(0) + koff[c]);
+            mma(sA[0], kf, qf[0][c]);
+            mma(sA[1], kf, qf[1][c]);
+        }
+        if (is_edge(0)) apply_mask(sA, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float x = kNegInf;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) x = fmaxf(x, fmaxf(sA[nb][r], sA[nb][r + 1]));
+            mx[nb] = x;
+        }
+        if (DROPOUT) draw_keep(keep_cur, 0);
+    }
+    __syncthreads();   // K buffer 0 is refilled in the first step
+
+    // ---- steady state, two steps per trip (buffer parities are constants).
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using HN = std::true_type;
+    using NN = std::false_type;
+    int t = 0;
+    for (; t + 2 < Tw; t += 2) {
+        step(I0{}, HN{}, sA, sB, mx, t);
+        step(I1{}, HN{}, sB, sA, mx, t + 1);
+    }
+    if (t + 1 < Tw) {          // two tiles left
+        step(I0{}, HN{}, sA, sB, mx, t);
+        step(I1{}, NN{}, sB, sA, mx, t + 1);
+        t += 2;
+    } else if (t < Tw) {       // one tile left
+        step(I0{}, NN{}, sA, sB, mx, t);
+        t += 1;
+    }
+    // Tiles beyond this wavefront's rows: keep the workgroup's loads and
+    // barriers in step.
+    for (; t < NT; ++t) {
+        load_tile(krs, t + 2, kbuf(t & 1));
+        load_tile(vrs, t + 1, vbuf((t + 1) & 1));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
