@@ -369,6 +369,34 @@ __device__ __forceinline__ void pin_agpr(V &x) { asm volatile("" : "+a"(x)); }
 template <typename V>
 __device__ __forceinline__ void pin_vgpr(V &x) { asm volatile("" : "+v"(x)); }
 
+// ------------------------------------------------------ packed 16-bit pairs
+
+// Two fp32 values rounded (RNE) into a packed pair of 16-bit values.
+template <typename T>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    t2 v;
+    v[0] = from_f32<T>(lo);
+    v[1] = from_f32<T>(hi);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// acc += lo + hi of a packed pair of 16-bit values (exact products with 1).
+template <typename T>
+__device__ __forceinline__ float sum2(uint32_t pair, float acc);
+template <>
+__device__ __forceinline__ float sum2<bf16>(uint32_t pair, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, pair), one, acc, false);
+}
+template <>
+__device__ __forceinline__ float sum2<f16>(uint32_t pair, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pair), one, acc, false);
+}
+
 // --------------------------------------------------------------- utilities
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

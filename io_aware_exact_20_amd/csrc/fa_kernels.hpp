@@ -44,6 +44,11 @@ hipError_t launch_bwd_dkdv(Elem e, int d, bool causal, bool dropout, const BwdAr
                            hipStream_t stream);
 hipError_t launch_bwd_dq(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                          hipStream_t stream);
+// 16-bit inputs only (bf16, f16).
+hipError_t launch_bwd_dq16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
+                           hipStream_t stream);
+hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
+                             hipStream_t stream);
 hipError_t launch_dropout_mask(int64_t N, uint32_t T, uint32_t seed_lo, uint32_t seed_hi,
                                int64_t b, int64_t h, uint8_t *mask, hipStream_t stream);
 
