@@ -345,8 +345,11 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
 // Q^T) are read from the row-major LDS tiles with ds_read_b64_tr_b16.
 //
 // A hands P over through LDS in fp32 (the register image of its
-// accumulator, lane for lane), with the sign bit set where the element is
-// dropped.  Per 32-row step t:
+// accumulator, lane for lane).  Dropout keep decisions are drawn once per
+// tile, half by each wavefront of the pair, as 16-bit masks in a row-major
+// LDS block; the transposed 16-bit LDS read hands every lane the masks of
+// its own (key, rows) registers, already paired as the products need them.
+// Per 32-row step t:
 //   A: S of tile t, P of tile t (to LDS), dV += dO^T (keep P) of tile t;
 //   B: dS of tile t-1 from its dP and A's P, dK += Q^T dS, dP of tile t;
 // so B reads A's P one step after it was written (one barrier per step).
@@ -385,7 +388,11 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     __shared__ __attribute__((aligned(256))) float lse_s[2][64];
     __shared__ __attribute__((aligned(256))) float dv_s[4][64];
     __shared__ __attribute__((aligned(1024))) float pex[2][2][32 * 64];   // [slot][pair][regs x lanes]
-    __shared__ __attribute__((aligned(16))) uint32_t keep_t[2][2][32];     // [pair][key block][row]
+    // Dropout keep masks: 16-bit 0x0000 / 0xFFFF per (row, key) of a pair's
+    // 32 x 64 block, row-major with a 192-byte row pitch (conflict-free for
+    // the transposed reads); four tiles in flight.
+    constexpr int MP = 192;
+    __shared__ __attribute__((aligned(1024))) char mk[DROPOUT ? 4 : 1][2][32 * MP];
     auto qbuf = [&](int s) {
         return s == 0 ? (lds_char *)qs0 : s == 1 ? (lds_char *)qs1 : s == 2 ? (lds_char *)qs2 : (lds_char *)qs3;
     };
@@ -496,6 +503,36 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         }
     };
 
+    // Keep masks of key block kb of this pair for tile t: lane (row lq,
+    // half g) draws the 16 keys 32kb + 16g .. +15 of its row (two Philox
+    // blocks) and stores them as 16-bit masks.
+    auto gen_masks = [&](int t, int kb, int slot) {
+        const uint32_t grp = (uint32_t)((kp0 + 32 * kb) >> 3) + 2 * g;
+        const uint32_t row = (uint32_t)((j0 + t) * BQ + lq);
+        FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + (32 * kb + 16 * g) * 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const Philox4 r = philox4x32_10(grp + h, row, h_idx, b_idx, a.seed_lo, a.seed_hi);
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)   // word q: keys 2q (low half), 2q + 1 (high half)
+                w[q] = ((r.x[q] & 0xFFFFu) >= a.drop_T ? 0x0000FFFFu : 0u) |
+                       ((r.x[q] >> 16) >= a.drop_T ? 0xFFFF0000u : 0u);
+            *(FA_LDS u32x4 *)(p + 16 * h) = w;
+        }
+    };
+    // Per-lane byte offset of the transposed mask read: lane receives the
+    // masks of rows 8 q4 + 4g + 0..3 (its registers 4 q4 .. 4 q4 + 3) of key
+    // 32 kb + lq, with q4 and kb added as immediates.
+    const uint32_t mtr = (uint32_t)((4 * ((lane >> 5)) + ((lane >> 2) & 3)) * MP +
+                                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+    auto read_masks = [&](int slot, int kb, int q4) {
+        const half_t<T> m = lds_half_tr<T>((lds_char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + mtr +
+                                           (uint32_t)(8 * q4 * MP + 32 * kb * 2));
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(u32x2, m);
+    };
+
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -519,44 +556,13 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     }
     if (role == 0) load_rows(0, (lds_char *)lse_s[0]);
     else load_rows(0, (lds_char *)dv_s[0]);
+    if (DROPOUT) gen_masks(0, role, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     if (role == 0) {
         // ============================== A: S, P, dV ==============================
         f32x16 sacc[2];
-        uint32_t keepw[2];   // bit r of keepw[kb]: register r of key block kb kept
-        // Keep bits of tile t for this lane's two keys, through LDS: lane
-        // (row lq, half g) draws two 8-key groups per key block.
-        auto draw_keep = [&](int t) {
-            const int qt0 = (j0 + t) * BQ;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const uint32_t grp = (uint32_t)((kp0 + 32 * kb) >> 3) + 2 * g;
-                const uint32_t row = (uint32_t)(qt0 + lq);
-                const uint32_t lo = keep_byte(grp, row, h_idx, b_idx, a.seed_lo, a.seed_hi, a.drop_T);
-                const uint32_t hi = keep_byte(grp + 1, row, h_idx, b_idx, a.seed_lo, a.seed_hi, a.drop_T);
-                ((FA_LDS uint16_t *)&keep_t[pair][kb][lq])[g] = (uint16_t)(lo | (hi << 8));
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                uint32_t bits = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 w4 = *(const FA_LDS u32x4 *)&keep_t[pair][kb][8 * i + 4 * g];
-                    bits |= ((w4[0] >> lq) & 1u) << (4 * i + 0);
-                    bits |= ((w4[1] >> lq) & 1u) << (4 * i + 1);
-                    bits |= ((w4[2] >> lq) & 1u) << (4 * i + 2);
-                    bits |= ((w4[3] >> lq) & 1u) << (4 * i + 3);
-                }
-                keepw[kb] = bits;
-            }
-            __builtin_amdgcn_wave_barrier();
-        };
-
         // Step s (R = s % 4): S of tile s (Q slot s%4), P of tile s, dV of
         // tile s (dO slot s%2); loads of tile s+1.
         auto a_step = [&](auto r_c, int s) {
@@ -566,7 +572,6 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             const FA_LDS float *lsep = (const FA_LDS float *)lse_s[R & 1];
             FA_LDS float *px = (FA_LDS float *)pex[R & 1][pair];
             issue_loads(s, (R + 1) & 3, (R + 1) & 1, (R + 1) & 1, 0);
-            if (DROPOUT) draw_keep(s);
 
             // ---- S = Q K^T.
             sacc[0] = f32x16{};
@@ -595,21 +600,15 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 for (int e = 0; e < 4; ++e)
                     pv[e] = fast_exp2(fmaf(sacc[kb][4 * q4 + e], sl2, -l4[e] * kLog2eB));
                 f32x4 xo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xo[e] = pv[e];
+                pp[kb][2 * q4] = pack2<T>(pv[0], pv[1]);
+                pp[kb][2 * q4 + 1] = pack2<T>(pv[2], pv[3]);
                 if (DROPOUT) {
-                    float pk[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool kept = (keepw[kb] >> (4 * q4 + e)) & 1u;
-                        pk[e] = kept ? pv[e] : 0.f;
-                        xo[e] = kept ? pv[e] : -pv[e];   // sign bit marks a dropped element
-                    }
-                    pp[kb][2 * q4] = pack2<T>(pk[0], pk[1]);
-                    pp[kb][2 * q4 + 1] = pack2<T>(pk[2], pk[3]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) xo[e] = pv[e];
-                    pp[kb][2 * q4] = pack2<T>(pv[0], pv[1]);
-                    pp[kb][2 * q4 + 1] = pack2<T>(pv[2], pv[3]);
+                    // keep P: the transposed mask read gives exactly these two pairs.
+                    const auto mw = read_masks(R, kb, q4);
+                    pp[kb][2 * q4] &= mw[0];
+                    pp[kb][2 * q4 + 1] &= mw[1];
                 }
                 *(FA_LDS f32x4 *)(px + (c * kWave + lane) * 4) = xo;
             }
@@ -632,6 +631,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                         mma(acc[db][kb], ot, __builtin_bit_cast(frag_t<T>, pv));
                     }
                 }
+            if (DROPOUT) gen_masks(s + 1, 0, R + 1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };
@@ -667,13 +667,20 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     const f32x4 d4 = *(const FA_LDS f32x4 *)(dvp + 8 * q4 + 4 * g);
                     const f32x4 x4 = *(const FA_LDS f32x4 *)(px + (c * kWave + lane) * 4);
                     float ds[4];
+                    uint32_t mw2[2] = {0xFFFFFFFFu, 0xFFFFFFFFu};
+                    if (DROPOUT) {
+                        const auto mw = read_masks(R + 3, kb, q4);
+                        mw2[0] = mw[0];
+                        mw2[1] = mw[1];
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const float dpv = dacc[kb][4 * q4 + e];
                         if (DROPOUT) {
-                            const float p = fabsf(x4[e]);
-                            const float kd = __builtin_signbit(x4[e]) ? 0.f : dpv * dc;
-                            ds[e] = p * (kd - d4[e]);
+                            // dP * keep * c: the 16-bit mask sign-extended to 32 bits.
+                            const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)mw2[e >> 1], 16 * (e & 1), 16);
+                            const float kd = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, dpv * dc) & m);
+                            ds[e] = x4[e] * (kd - d4[e]);
                         } else {
                             ds[e] = x4[e] * (dpv - d4[e]);
                         }
@@ -713,6 +720,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     mma(dacc[0], of[c % 3], kv[0][c]);
                     mma(dacc[1], of[c % 3], kv[1][c]);
                 }
+                if (DROPOUT) gen_masks(s + 1, 1, R + 1);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
