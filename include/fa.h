@@ -100,8 +100,8 @@ fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const voi
 
 /*
  * Bytes of device workspace fa_bwd needs for `p` (0 for an empty problem,
- * (size_t)-1 for invalid parameters): the fp32 row dot-products
- * D_i = dO_i . O_i, [B,H,N], rounded up to 256 bytes.
+ * (size_t)-1 for invalid parameters): two fp32 arrays of B*H*N row
+ * statistics (see fa_bwd_prepare), each rounded up to 256 bytes.
  */
 size_t fa_bwd_workspace_bytes(const fa_params_t *p);
 
@@ -122,14 +122,17 @@ fa_status_t fa_bwd(const fa_params_t *p, const void *q, const void *k, const voi
  * The backward as three stages, in the order fa_bwd enqueues them (all on
  * one stream; later stages read the D_i the first one leaves in
  * `workspace`):
- *   fa_bwd_prepare  D_i = dO_i . O_i (fp32) into the workspace;
+ *   fa_bwd_prepare  per query row i, in fp32 into the workspace: D_i / c
+ *                   (D_i = dO_i . O_i, c = 1/(1-dropout_p), 1 without
+ *                   dropout) and -lse_i log2(e); the later stages fold c
+ *                   into their outputs;
  *   fa_bwd_dkdv     recomputes S and P tile by tile per key block and writes
  *                   dK and dV;
  *   fa_bwd_dq       recomputes S and P tile by tile per query block and
  *                   writes dQ (no atomics: results are deterministic).
  * Arguments mean the same as in fa_bwd; each stage validates its own.
  */
-fa_status_t fa_bwd_prepare(const fa_params_t *p, const void *o, const void *dout,
+fa_status_t fa_bwd_prepare(const fa_params_t *p, const void *o, const float *lse, const void *dout,
                            void *workspace, size_t workspace_bytes, void *stream);
 fa_status_t fa_bwd_dkdv(const fa_params_t *p, const void *q, const void *k, const void *v,
                         const float *lse, const void *dout, void *dk, void *dv,

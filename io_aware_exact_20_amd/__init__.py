@@ -62,7 +62,7 @@ def load():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fa_bwd.restype = ctypes.c_int
-    lib.fa_bwd_prepare.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.fa_bwd_prepare.argtypes = [P, vp, vp, vp, vp, sz, vp]
     lib.fa_bwd_prepare.restype = ctypes.c_int
     lib.fa_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.fa_bwd_dkdv.restype = ctypes.c_int
@@ -187,8 +187,8 @@ class Problem:
                            _ptr(self.o), _ptr(self.lse), self._s))
 
     def bwd_prepare(self):
-        _check(_lib.fa_bwd_prepare(ctypes.byref(self.p), _ptr(self.o), _ptr(self.dout),
-                                   _ptr(self.ws), self.ws.numel(), self._s))
+        _check(_lib.fa_bwd_prepare(ctypes.byref(self.p), _ptr(self.o), _ptr(self.lse),
+                                   _ptr(self.dout), _ptr(self.ws), self.ws.numel(), self._s))
 
     def bwd_dkdv(self):
         _check(_lib.fa_bwd_dkdv(ctypes.byref(self.p), _ptr(self.q), _ptr(self.k), _ptr(self.v),

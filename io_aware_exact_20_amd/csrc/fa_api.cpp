@@ -74,11 +74,14 @@ fa::Elem elem(int32_t dtype) {
 uint32_t drop_threshold(float p) { return (uint32_t)std::llround((double)p * 65536.0); }
 float keep_scale(float p) { return (float)(1.0 / (1.0 - (double)p)); }
 
-size_t workspace_bytes(const fa_params_t *p) {
-    // The fp32 row dot-products D_i, padded to 256 bytes.
+// The workspace holds two fp32 arrays of one value per query row, each
+// padded to 256 bytes: D_i / c, then -lse_i log2(e).
+size_t row_array_bytes(const fa_params_t *p) {
     const size_t rows = (size_t)p->B * (size_t)p->H * (size_t)p->N;
     return (rows * 4 + 255) / 256 * 256;
 }
+
+size_t workspace_bytes(const fa_params_t *p) { return 2 * row_array_bytes(p); }
 
 fa_status_t hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess)
@@ -126,7 +129,7 @@ size_t fa_bwd_workspace_bytes(const fa_params_t *p) {
 namespace {
 
 // Common part of the backward entry points: parameter and workspace checks,
-// and the argument block (the workspace holds D).
+// and the argument block (the workspace holds the two row arrays).
 fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t workspace_size,
                       bool *empty, fa::BwdArgs *a) {
     fa_status_t s = check_params(p, empty);
@@ -138,6 +141,8 @@ fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t worksp
                     workspace_size, need);
     *a = fa::BwdArgs{};
     a->dvec = reinterpret_cast<float *>(const_cast<void *>(workspace));
+    a->nl2 = reinterpret_cast<float *>(reinterpret_cast<char *>(const_cast<void *>(workspace)) +
+                                       row_array_bytes(p));
     a->B = p->B; a->H = p->H; a->N = p->N;
     a->scale = p->scale;
     a->scale_log2 = p->scale * 1.44269504088896340736f;
@@ -154,15 +159,16 @@ fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t worksp
 
 extern "C" {
 
-fa_status_t fa_bwd_prepare(const fa_params_t *p, const void *o, const void *dout,
+fa_status_t fa_bwd_prepare(const fa_params_t *p, const void *o, const float *lse, const void *dout,
                            void *workspace, size_t workspace_size, void *stream) {
     bool empty = false;
     fa::BwdArgs a;
     fa_status_t s = bwd_setup(p, workspace, workspace_size, &empty, &a);
     if (s != FA_OK) return s;
     if (empty) return ok();
-    if ((s = check_ptr(o, "o")) || (s = check_ptr(dout, "dout"))) return s;
-    a.o = o; a.dout = dout;
+    if ((s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")) || (s = check_ptr(dout, "dout")))
+        return s;
+    a.o = o; a.lse = lse; a.dout = dout;
     return hip_status(fa::launch_bwd_pre(elem(p->dtype), (int)p->d, a,
                                          reinterpret_cast<hipStream_t>(stream)),
                       "fa_bwd_prepare launch");
@@ -218,7 +224,7 @@ fa_status_t fa_bwd(const fa_params_t *p, const void *q, const void *k, const voi
         (s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")) || (s = check_ptr(dout, "dout")) ||
         (s = check_ptr(dq, "dq")) || (s = check_ptr(dk, "dk")) || (s = check_ptr(dv, "dv")))
         return s;
-    if ((s = fa_bwd_prepare(p, o, dout, workspace, workspace_size, stream))) return s;
+    if ((s = fa_bwd_prepare(p, o, lse, dout, workspace, workspace_size, stream))) return s;
     if ((s = fa_bwd_dkdv(p, q, k, v, lse, dout, dk, dv, workspace, workspace_size, stream)))
         return s;
     return fa_bwd_dq(p, q, k, v, lse, dout, dq, workspace, workspace_size, stream);

@@ -38,7 +38,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 // ------------------------------------------------------------- preprocess
 
-// D_i = sum_c dO_ic O_ic in fp32.  16 lanes per row.
+// Row statistics of the backward, one value per query row in fp32:
+// D_i / c with D_i = sum_c dO_ic O_ic and c the dropout keep scale (1
+// without dropout), and -lse_i log2(e).  With D_i / c the dS of every
+// kernel is dS / c = P o (keep dP - D / c), and c joins the scale of dK and
+// dQ.  16 lanes per row.
 template <typename T, typename TO, int D>
 __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a, int64_t rows) {
     const int64_t row = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
@@ -53,7 +57,10 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a, int64_t r
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (row < rows && sub == 0) a.dvec[row] = acc;
+    if (row < rows && sub == 0) {
+        a.dvec[row] = acc / a.drop_c;
+        a.nl2[row] = -a.lse[row] * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -201,7 +208,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
                 if (DROPOUT) {
                     const bool kept = (keepw[r] >> lq) & 1u;
                     pkv = kept ? p : 0.f;
-                    dpv = kept ? dpv * a.drop_c : 0.f;
+                    dpv = kept ? dpv : 0.f;
                 }
                 pk[r] = pkv;
                 ds[r] = p * (dpv - dvec_s[buf][qi]);
@@ -225,9 +232,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
         __syncthreads();
     }
 
-    // ---- dK = scale * dK^T^T, dV = c * dV^T^T.  Register r of block db is
+    // ---- dK = scale c (dK/c)^T^T, dV = c dV^T^T.  Register r of block db is
     // column 32 db + 8(r/4) + 4g + r%4 of the lane's key row.
     const float vscale = DROPOUT ? a.drop_c : 1.f;
+    const float kscale = DROPOUT ? a.scale * a.drop_c : a.scale;
     if (key < N) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -236,8 +244,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
                 const int col = 32 * db + 8 * rr + 4 * g;
                 const float v0 = vscale * dv_acc[db][4 * rr], v1 = vscale * dv_acc[db][4 * rr + 1];
                 const float v2 = vscale * dv_acc[db][4 * rr + 2], v3 = vscale * dv_acc[db][4 * rr + 3];
-                const float s0 = a.scale * dk_acc[db][4 * rr], s1 = a.scale * dk_acc[db][4 * rr + 1];
-                const float s2 = a.scale * dk_acc[db][4 * rr + 2], s3 = a.scale * dk_acc[db][4 * rr + 3];
+                const float s0 = kscale * dk_acc[db][4 * rr], s1 = kscale * dk_acc[db][4 * rr + 1];
+                const float s2 = kscale * dk_acc[db][4 * rr + 2], s3 = kscale * dk_acc[db][4 * rr + 3];
                 if (a.out_f32) {
                     store4<float>(reinterpret_cast<float *>(a.dv) + head + key * D + col, v0, v1, v2, v3);
                     store4<float>(reinterpret_cast<float *>(a.dk) + head + key * D + col, s0, s1, s2, s3);
@@ -353,7 +361,7 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
                     if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
                 }
                 float dpv = dp[r];
-                if (DROPOUT) dpv = ((keep >> r) & 1u) ? dpv * a.drop_c : 0.f;
+                if (DROPOUT) dpv = ((keep >> r) & 1u) ? dpv : 0.f;
                 ds[r] = p * (dpv - dvec);
             }
             // dQ^T += K^T dS^T; K^T fragments come from the row-major K tile.
@@ -373,14 +381,15 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
         __syncthreads();
     }
 
+    const float qscale = DROPOUT ? a.scale * a.drop_c : a.scale;
     if (qrow < N) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int col = 32 * db + 8 * rr + 4 * g;
-                const float x0 = a.scale * acc[db][4 * rr + 0], x1 = a.scale * acc[db][4 * rr + 1];
-                const float x2 = a.scale * acc[db][4 * rr + 2], x3 = a.scale * acc[db][4 * rr + 3];
+                const float x0 = qscale * acc[db][4 * rr + 0], x1 = qscale * acc[db][4 * rr + 1];
+                const float x2 = qscale * acc[db][4 * rr + 2], x3 = qscale * acc[db][4 * rr + 3];
                 if (a.out_f32) store4<float>(reinterpret_cast<float *>(a.dq) + head + qrow * D + col, x0, x1, x2, x3);
                 else store4<T>(reinterpret_cast<T *>(a.dq) + head + qrow * D + col, x0, x1, x2, x3);
             }

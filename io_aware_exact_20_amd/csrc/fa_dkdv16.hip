@@ -1,0 +1,565 @@
+// Backward of fused exact attention for 16-bit inputs on gfx950: the dK /
+// dV pass.
+//
+// The scores and probabilities are recomputed from Q, K and the stored
+// log-sum-exp ("Recomputation", mrodiduger.github.io page).  With
+//
+//   S = scale Q K^T,  P = exp(S - LSE),  dP = (dO V^T) * keep * c,
+//   D_i = dO_i . O_i,  dS = P o (dP - D),
+//
+// this kernel produces dV = (keep c P)^T dO and dK = scale dS^T Q for one
+// block of keys per workgroup, streaming the query sequence.
+//
+// All matrix products of this file keep their accumulators in AGPRs (the
+// accumulation registers): the two 128 x 64 accumulators, the K or V
+// operands and the double-buffered scores of a wavefront fill the 256 AGPRs
+// at d = 128, and the ordinary VGPRs are left for the exponentials, the
+// rounded operands and LDS reads issued two groups ahead of their use.
+#include <type_traits>
+
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// One workgroup owns 128 keys: two pairs of wavefronts, each pair 64 keys.
+// The four products of the backward are split between the two wavefronts
+// of a pair, so that each holds only one 128x64 accumulator (dV^T or dK^T,
+// keys along the lanes) besides its operands:
+//   A: S = Q K^T (K of its keys in AGPRs), P = exp(S - LSE) and the keep
+//      bits, then dV^T += dO^T (keep P);
+//   B: dP = dO V^T (V in AGPRs), dS = P o (dP keep c - D) with P taken from
+//      A, then dK^T += Q^T dS.
+// Both products of a wavefront contract over the 32 query rows of a step
+// with the keys on the accumulator columns, so the rounded S / dS
+// registers are directly their B operands; the transposed A operands (dO^T,
+// Q^T) are read from the row-major LDS tiles with ds_read_b64_tr_b16.
+//
+// A hands P over through LDS in fp32 (the register image of its
+// accumulator, lane for lane).  Dropout keep decisions are drawn once per
+// tile, half by each wavefront of the pair, as 16-bit masks in a row-major
+// LDS block; the transposed 16-bit LDS read hands every lane the masks of
+// its own (key, rows) registers, already paired as the products need them.
+// Per 32-row step t:
+//   A: S of tile t+1 | P of tile t (to LDS);  dV += dO^T (keep P) of tile t;
+//   B: dP of tile t | dS of tile t-1;         dK += Q^T dS of tile t-1;
+// ("x | y": products x on the matrix cores while the VALU does y), so B
+// reads A's P one step after it was written (one barrier per step).  Tile
+// t's Q is read by A in step t-1 and by B in step t+1 (four LDS buffers);
+// dO tiles are read in one step (two buffers).
+template <typename T, int D>
+struct Dkdv16Tile {
+    static constexpr int NW = 4;                       // 2 pairs x (A, B)
+    static constexpr int KP = 64;                      // keys per pair
+    static constexpr int BK = 2 * KP;                  // keys per workgroup
+    static constexpr int BQ = 32;                      // query rows per step
+    static constexpr int THREADS = NW * kWave;
+    static constexpr int TB = BQ * D * 2;              // bytes of a Q or dO tile
+    static constexpr int LOADS = TB / (kWave * 16) / NW;
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 4 bytes per lane at byte offset voff + soff straight into LDS at base + 4 l.
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         lds_char *base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void *)base, 4, voff, soff, 0, 0);
+}
+
+template <typename T, int D, bool CAUSAL, bool DROPOUT>
+__global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
+    using TL = Dkdv16Tile<T, D>;
+    using SW = Swz<D>;
+    constexpr int NW = TL::NW, KP = TL::KP, BK = TL::BK, BQ = TL::BQ;
+    constexpr int TB = TL::TB, LOADS = TL::LOADS;
+    constexpr int RB = SW::ROW_BYTES;
+    constexpr int NDC = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr float kNegInf = -__builtin_huge_valf();
+    static_assert(LOADS >= 1, "tile load split");
+
+    __shared__ __attribute__((aligned(1024))) char qs0[TB], qs1[TB], qs2[TB], qs3[TB], os0[TB], os1[TB];
+    __shared__ __attribute__((aligned(256))) float nl_s[2][64];
+    __shared__ __attribute__((aligned(256))) float dv_s[4][64];
+    __shared__ __attribute__((aligned(1024))) float pex[2][2][32 * 64];   // [slot][pair][regs x lanes]
+    // Dropout keep masks: 16-bit 0x0000 / 0xFFFF per (row, key) of a pair's
+    // 32 x 64 block, row-major with a 192-byte row pitch (conflict-free for
+    // the transposed reads); four tiles in flight.
+    constexpr int MP = 192;
+    __shared__ __attribute__((aligned(1024))) char mk[DROPOUT ? 4 : 1][2][32 * MP];
+    auto qbuf = [&](int s) {
+        return s == 0 ? (lds_char *)qs0 : s == 1 ? (lds_char *)qs1 : s == 2 ? (lds_char *)qs2 : (lds_char *)qs3;
+    };
+    auto obuf = [&](int s) { return s == 0 ? (lds_char *)os0 : (lds_char *)os1; };
+
+    const int lane = (int)lane_in_wave();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int role = wave >> 1, pair = wave & 1;          // role 0: A, 1: B
+    const int lq = lane & 31, g = lane >> 5;
+
+    const int64_t BH = a.B * a.H;
+    const int64_t u = blockIdx.x;
+    const int64_t bh = u % BH;
+    const int kblk = (int)(u / BH);                       // causal: low key blocks (most work) first
+    const int N = (int)a.N;
+    const size_t head = (size_t)bh * (size_t)N * D;
+    const T *__restrict__ Qg = reinterpret_cast<const T *>(a.q) + head;
+    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head;
+    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ dOg = reinterpret_cast<const T *>(a.dout) + head;
+    const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
+
+    const int k0 = kblk * BK;                 // first key of the workgroup
+    const int kp0 = k0 + pair * KP;           // first key of this pair
+    const int j0 = CAUSAL ? k0 / BQ : 0;      // first query tile
+    const int NTQ = (N + BQ - 1) / BQ - j0;   // query tiles streamed
+
+    // ---- the pair's K (A) or V (B) rows: B operands, one key per lane, in AGPRs.
+    frag_t<T> kv[2][NDC];
+    {
+        const T *src = role == 0 ? Kg : Vg;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            int key = kp0 + 32 * kb + lq;
+            key = key < N ? key : N - 1;
+#pragma unroll
+            for (int c = 0; c < NDC; ++c) {
+                kv[kb][c] = load_frag<T>(src + (size_t)key * D + 16 * c + 8 * g);
+                pin_agpr(kv[kb][c]);
+            }
+        }
+    }
+
+    // ---- LDS offsets: row fragments of a Q / dO tile (row = query lq) and
+    // transposed reads (rows = queries, columns = d).
+    uint32_t roff[NDC];
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) roff[c] = SW::off(lq, 16 * c + 8 * g);
+    uint32_t toff[2][NDB];
+    {
+        const int G = lane >> 4, k = (lane >> 2) & 3, j = lane & 3;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                toff[hf][db] = SW::off(8 * hf + 4 * (G >> 1) + k, 32 * db + 16 * (G & 1) + 4 * j);
+    }
+
+    // ---- loads: Q and dO tiles (all four wavefronts, LOADS instructions
+    // each), -LSE log2(e) rows (the A wavefronts) and D/c rows (the B
+    // wavefronts).
+    constexpr int RSTEP = NW * kWave / SW::CPR;
+    const int R0 = (wave * kWave + lane) / SW::CPR;
+    const uint32_t gcol = (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0)) * 8);
+    const uint32_t lane_boff = ((uint32_t)R0 * D + gcol) * 2;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, head_bytes), ors = make_rsrc(dOg, head_bytes);
+    const __amdgpu_buffer_rsrc_t rrs =
+        role == 0 ? make_rsrc(a.nl2 + (size_t)bh * (size_t)N, (uint32_t)N * 4)
+                  : make_rsrc(a.dvec + (size_t)bh * (size_t)N, (uint32_t)N * 4);
+    auto load_tile_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
+        buf2lds16(rs, lane_boff, (uint32_t)(((j0 + t) * BQ + i * RSTEP) * D * 2),
+                  buf + (wave + i * NW) * (kWave * 16));
+    };
+    auto load_rows = [&](int t, lds_char *buf) {   // 64 fp32 rows from the tile's first row
+        buf2lds4(rrs, (uint32_t)lane * 4, (uint32_t)((j0 + t) * BQ) * 4, buf);
+    };
+    // Loads issued during step s: Q of tile s+2; dO and row statistics of tile s+1.
+    auto issue_loads = [&](int s, int qsl, int osl, int rsl2, int rsl4) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            load_tile_part(qrs, s + 2, qbuf(qsl), i);
+            load_tile_part(ors, s + 1, obuf(osl), i);
+        }
+        if (role == 0) load_rows(s + 1, (lds_char *)nl_s[rsl2]);
+        else load_rows(s + 1, (lds_char *)dv_s[rsl4]);
+    };
+
+    const float sl2 = a.scale_log2, dc = a.drop_c;
+    f32x16 acc[NDB][2];          // dV^T (A) or dK^T (B): [d block][key block]
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { acc[db][0] = f32x16{}; acc[db][1] = f32x16{}; }
+
+    // Masking of tile t for this pair: key > query (causal), key >= N, row >= N.
+    auto is_edge = [&](int t) {
+        const int qt0 = (j0 + t) * BQ;
+        return (qt0 + BQ > N) || (kp0 + KP > N) || (CAUSAL && kp0 + KP - 1 > qt0);
+    };
+    auto apply_mask = [&](f32x16 (&s)[2], int t) {
+        const int qt0 = (j0 + t) * BQ;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = kp0 + 32 * kb + lq;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int q = qt0 + 8 * (r / 4) + 4 * g + (r % 4);
+                if ((CAUSAL && key > q) || key >= N || q >= N) s[kb][r] = kNegInf;
+            }
+        }
+    };
+
+    // Keep masks of key block kb of this pair for tile t: lane (row lq,
+    // half g) draws the 16 keys 32kb + 16g .. +15 of its row (two Philox
+    // blocks) and stores them as 16-bit masks.
+    auto gen_masks = [&](int t, int kb, int slot) {
+        const uint32_t grp = (uint32_t)((kp0 + 32 * kb) >> 3) + 2 * g;
+        const uint32_t row = (uint32_t)((j0 + t) * BQ + lq);
+        FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + (32 * kb + 16 * g) * 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const Philox4 r = philox4x32_10(grp + h, row, h_idx, b_idx, a.seed_lo, a.seed_hi);
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)   // word q: keys 2q (low half), 2q + 1 (high half)
+                w[q] = ((r.x[q] & 0xFFFFu) >= a.drop_T ? 0x0000FFFFu : 0u) |
+                       ((r.x[q] >> 16) >= a.drop_T ? 0xFFFF0000u : 0u);
+            *(FA_LDS u32x4 *)(p + 16 * h) = w;
+        }
+    };
+    // Per-lane byte offset of the transposed mask read: lane receives the
+    // masks of rows 8 q4 + 4g + 0..3 (its registers 4 q4 .. 4 q4 + 3) of key
+    // 32 kb + lq, with q4 and kb added as immediates.
+    const uint32_t mtr = (uint32_t)((4 * ((lane >> 5)) + ((lane >> 2) & 3)) * MP +
+                                    (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2);
+    auto read_masks = [&](int slot, int kb, int q4) {
+        const half_t<T> m = lds_half_tr<T>((lds_char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + mtr +
+                                           (uint32_t)(8 * q4 * MP + 32 * kb * 2));
+        return __builtin_bit_cast(u32x2, m);
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using YES = std::true_type;
+    using NO = std::false_type;
+    auto dispatch4 = [&](int r, auto f) {
+        switch (r & 3) {
+        case 0: f(I0{}); break;
+        case 1: f(I1{}); break;
+        case 2: f(I2{}); break;
+        default: f(I3{}); break;
+        }
+    };
+
+    // ---- prologue loads: Q_0, Q_1, dO_0, rows of tile 0.
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        load_tile_part(qrs, 0, qbuf(0), i);
+        load_tile_part(qrs, 1, qbuf(1), i);
+        load_tile_part(ors, 0, obuf(0), i);
+    }
+    if (role == 0) load_rows(0, (lds_char *)nl_s[0]);
+    else load_rows(0, (lds_char *)dv_s[0]);
+    if (DROPOUT) gen_masks(0, role, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Work of one step is laid out in groups of two matrix products each
+    // (sched_barrier between groups), with the VALU work of the group
+    // placed between its two products and every LDS read issued two groups
+    // before the group that uses it.
+    if (role == 0) {
+        // ============================== A: S, P, dV ==============================
+        // Step s: S of tile s+1 (Q slot (s+1)%4) on the matrix cores while
+        // the VALU exponentiates tile s; then dV of tile s (dO slot s%2).
+        f32x16 sA[2], sB[2];
+        auto a_step = [&](auto r_c, f32x16 (&sc)[2], f32x16 (&sn)[2], int s) {
+            constexpr int R = decltype(r_c)::value;
+            lds_char *qb = qbuf((R + 1) & 3);
+            lds_char *ob = obuf(R & 1);
+            const FA_LDS float *nlp = (const FA_LDS float *)nl_s[R & 1];
+            FA_LDS float *px = (FA_LDS float *)pex[R & 1][pair];
+            issue_loads(s, (R + 2) & 3, (R + 1) & 1, (R + 1) & 1, 0);
+
+            frag_t<T> qf[3], of[3];
+            qf[0] = lds_frag<T>(qb + roff[0]);
+            qf[1] = lds_frag<T>(qb + roff[1]);
+            f32x4 l4[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) l4[q4] = *(const FA_LDS f32x4 *)(nlp + 8 * q4 + 4 * g);
+            u32x2 mw[2][4];
+            if (DROPOUT) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) mw[kb][q4] = read_masks(R, kb, q4);
+            }
+            float pv[2][4][4];
+            uint32_t pp[2][8];
+            // P of register group (kb, q4) of tile s, also handed to B in fp32.
+            auto pgroup = [&](int kb, int q4) {
+                f32x4 xo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = fast_exp2(fmaf(sc[kb][4 * q4 + e], sl2, l4[q4][e]));
+                    pv[kb][q4][e] = p;
+                    xo[e] = p;
+                }
+                *(FA_LDS f32x4 *)(px + ((4 * kb + q4) * kWave + lane) * 4) = xo;
+            };
+            // Rounded (and kept) P of rows 8 q4 + .. for both key blocks.
+            auto ppair = [&](int q4) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    pp[kb][2 * q4] = pack2<T>(pv[kb][q4][0], pv[kb][q4][1]);
+                    pp[kb][2 * q4 + 1] = pack2<T>(pv[kb][q4][2], pv[kb][q4][3]);
+                    if (DROPOUT) {
+                        pp[kb][2 * q4] &= mw[kb][q4][0];
+                        pp[kb][2 * q4 + 1] &= mw[kb][q4][1];
+                    }
+                    pin_vgpr(pp[kb][2 * q4]);
+                    pin_vgpr(pp[kb][2 * q4 + 1]);
+                }
+            };
+            auto ofrag = [&](int j) {
+                const int cc = j / NDB, db = j % NDB;
+                const uint32_t kc_off = (uint32_t)(16 * cc * RB);
+                return join<T>(lds_half_tr<T>(ob + kc_off + toff[0][db]),
+                               lds_half_tr<T>(ob + kc_off + toff[1][db]));
+            };
+
+            // ---- phase 1: S of tile s+1 | P of tile s.
+            sn[0] = f32x16{};
+            sn[1] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NDC; ++c) {
+                if (c + 2 < NDC) qf[(c + 2) % 3] = lds_frag<T>(qb + roff[c + 2]);
+                if (c == NDC - 2) of[0] = ofrag(0);
+                if (c == NDC - 1) of[1] = ofrag(1);
+                mma(sn[0], qf[c % 3], kv[0][c]);
+                if (NDC == 8) {
+                    if (c < 6) pgroup(c & 1, c >> 1);     // q4 = 0, 1, 2
+                    else ppair(c - 6);                    // pairs of q4 = 0, 1
+                } else {
+                    pgroup(0, c);
+                    pgroup(1, c);
+                    ppair(c);
+                }
+                mma(sn[1], qf[c % 3], kv[1][c]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- phase 2: dV^T += dO^T (keep P) of tile s.
+#pragma unroll
+            for (int j = 0; j < 2 * NDB; ++j) {
+                const int cc = j / NDB, db = j % NDB;
+                if (j + 2 < 2 * NDB) of[(j + 2) % 3] = ofrag(j + 2);
+                if (NDC == 8) {
+                    if (j == 0) pgroup(0, 3);
+                    if (j == 1) pgroup(1, 3);
+                    if (j == 2) ppair(2);
+                    if (j == 3) ppair(3);
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    u32x4 p4;
+                    p4[0] = pp[kb][4 * cc + 0];
+                    p4[1] = pp[kb][4 * cc + 1];
+                    p4[2] = pp[kb][4 * cc + 2];
+                    p4[3] = pp[kb][4 * cc + 3];
+                    mma(acc[db][kb], of[j % 3], __builtin_bit_cast(frag_t<T>, p4));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (is_edge(s + 1)) apply_mask(sn, s + 1);
+            if (DROPOUT) gen_masks(s + 1, 0, R + 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+
+        // prologue: S of tile 0 (Q slot 0).
+        if (NTQ > 0) {
+            sA[0] = f32x16{};
+            sA[1] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NDC; ++c) {
+                const frag_t<T> qfr = lds_frag<T>(qbuf(0) + roff[c]);
+                mma(sA[0], qfr, kv[0][c]);
+                mma(sA[1], qfr, kv[1][c]);
+            }
+            if (is_edge(0)) apply_mask(sA, 0);
+        }
+        // The last step also computes S of tile NTQ (zero-filled rows past
+        // the end, never used), which keeps a single step shape.
+        for (int s = 0; s < NTQ; s += 4) {
+            a_step(I0{}, sA, sB, s);
+            if (s + 1 < NTQ) a_step(I1{}, sB, sA, s + 1);
+            if (s + 2 < NTQ) a_step(I2{}, sA, sB, s + 2);
+            if (s + 3 < NTQ) a_step(I3{}, sB, sA, s + 3);
+        }
+        // step NTQ: B finishes the last tile; keep the barrier count.
+        __syncthreads();
+    } else {
+        // ============================== B: dP, dS, dK ============================
+        // Step s: dP of tile s (dO slot s%2) on the matrix cores while the
+        // VALU forms dS of tile s-1 from its dP, A's P (P slot (s-1)%2) and D
+        // (D slot (s-1)%4); then dK of tile s-1 (Q slot (s-1)%4).
+        f32x16 dA[2], dB[2];
+        constexpr int IPG = 8 / NDC;     // dS register groups per product group
+        auto b_step = [&](auto r_c, auto hp_c, f32x16 (&dcur)[2], f32x16 (&dprv)[2], int s) {
+            constexpr int R = decltype(r_c)::value;
+            constexpr bool HP = decltype(hp_c)::value;
+            lds_char *ob = obuf(R & 1);
+            lds_char *qb = qbuf((R + 3) & 3);
+            const FA_LDS float *dvp = (const FA_LDS float *)dv_s[(R + 3) & 3];
+            const FA_LDS float *px = (const FA_LDS float *)pex[(R + 1) & 1][pair];
+            issue_loads(s, (R + 2) & 3, (R + 1) & 1, 0, (R + 1) & 3);
+
+            frag_t<T> of[3], qt[3];
+            of[0] = lds_frag<T>(ob + roff[0]);
+            of[1] = lds_frag<T>(ob + roff[1]);
+            f32x4 d4[4], x4[8];
+            u32x2 mw[8];
+            // item i = register group (kb, q4) = (i & 1, i >> 1)
+            auto fetch = [&](int i) {
+                x4[i] = *(const FA_LDS f32x4 *)(px + ((4 * (i & 1) + (i >> 1)) * kWave + lane) * 4);
+                if (DROPOUT) mw[i] = read_masks(R + 3, i & 1, i >> 1);
+            };
+            if (HP) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) d4[q4] = *(const FA_LDS f32x4 *)(dvp + 8 * q4 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 2 * IPG; ++i) fetch(i);
+            }
+            uint32_t sp[2][8];
+            auto dsitem = [&](int i) {
+                const int kb = i & 1, q4 = i >> 1;
+                const f32x4 x = x4[i];
+                float ds[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float dpv = dprv[kb][4 * q4 + e];
+                    if (DROPOUT) {
+                        // dP * keep: the 16-bit mask sign-extended to 32 bits.
+                        const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)mw[i][e >> 1], 16 * (e & 1), 16);
+                        const float kd = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, dpv) & m);
+                        ds[e] = x[e] * (kd - d4[q4][e]);
+                    } else {
+                        ds[e] = x[e] * (dpv - d4[q4][e]);
+                    }
+                }
+                sp[kb][2 * q4] = pack2<T>(ds[0], ds[1]);
+                sp[kb][2 * q4 + 1] = pack2<T>(ds[2], ds[3]);
+                pin_vgpr(sp[kb][2 * q4]);
+                pin_vgpr(sp[kb][2 * q4 + 1]);
+            };
+            auto qfrag = [&](int j) {
+                const int cc = j / NDB, db = j % NDB;
+                const uint32_t kc_off = (uint32_t)(16 * cc * RB);
+                return join<T>(lds_half_tr<T>(qb + kc_off + toff[0][db]),
+                               lds_half_tr<T>(qb + kc_off + toff[1][db]));
+            };
+
+            // ---- phase 1: dP of tile s | dS of tile s-1.
+            dcur[0] = f32x16{};
+            dcur[1] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NDC; ++c) {
+                if (c + 2 < NDC) of[(c + 2) % 3] = lds_frag<T>(ob + roff[c + 2]);
+                if (HP) {
+#pragma unroll
+                    for (int i = IPG * (c + 2); i < IPG * (c + 3); ++i)
+                        if (i < 8) fetch(i);
+                    if (c == NDC - 2) qt[0] = qfrag(0);
+                    if (c == NDC - 1) qt[1] = qfrag(1);
+                }
+                mma(dcur[0], of[c % 3], kv[0][c]);
+                if (HP) {
+#pragma unroll
+                    for (int i = IPG * c; i < IPG * (c + 1); ++i) dsitem(i);
+                }
+                mma(dcur[1], of[c % 3], kv[1][c]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- phase 2: dK^T += Q^T dS of tile s-1.
+            if (HP) {
+#pragma unroll
+                for (int j = 0; j < 2 * NDB; ++j) {
+                    const int cc = j / NDB, db = j % NDB;
+                    if (j + 2 < 2 * NDB) qt[(j + 2) % 3] = qfrag(j + 2);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        u32x4 p4;
+                        p4[0] = sp[kb][4 * cc + 0];
+                        p4[1] = sp[kb][4 * cc + 1];
+                        p4[2] = sp[kb][4 * cc + 2];
+                        p4[3] = sp[kb][4 * cc + 3];
+                        mma(acc[db][kb], qt[j % 3], __builtin_bit_cast(frag_t<T>, p4));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (DROPOUT) gen_masks(s + 1, 1, R + 1);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        };
+
+        // Steps 0 .. NTQ.  Step NTQ finishes tile NTQ-1; its dP half runs on
+        // the zero-filled rows past the last tile (harmless, never used).
+        if (NTQ > 0) {
+            b_step(I0{}, NO{}, dA, dB, 0);
+            for (int s = 1; s <= NTQ; s += 4) {
+                b_step(I1{}, YES{}, dB, dA, s);
+                if (s + 1 <= NTQ) b_step(I2{}, YES{}, dA, dB, s + 1);
+                if (s + 2 <= NTQ) b_step(I3{}, YES{}, dB, dA, s + 2);
+                if (s + 3 <= NTQ) b_step(I0{}, YES{}, dA, dB, s + 3);
+            }
+        } else {
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: dV = c * acc (A), dK = scale * acc (B); keys past N not stored.
+    const float osc = DROPOUT ? (role == 0 ? dc : a.scale * dc) : (role == 0 ? 1.f : a.scale);
+    void *dst = role == 0 ? a.dv : a.dk;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int key = kp0 + 32 * kb + lq;
+        if (key < N) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int col = 32 * db + 8 * rr + 4 * g;
+                    const float x0 = osc * acc[db][kb][4 * rr + 0], x1 = osc * acc[db][kb][4 * rr + 1];
+                    const float x2 = osc * acc[db][kb][4 * rr + 2], x3 = osc * acc[db][kb][4 * rr + 3];
+                    if (a.out_f32)
+                        store4<float>(reinterpret_cast<float *>(dst) + head + (size_t)key * D + col, x0, x1, x2, x3);
+                    else
+                        store4<T>(reinterpret_cast<T *>(dst) + head + (size_t)key * D + col, x0, x1, x2, x3);
+                }
+        }
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_dkdv16_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
+    using TL = Dkdv16Tile<T, D>;
+    const int64_t units = a.B * a.H * ((a.N + TL::BK - 1) / TL::BK);
+    if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)units), block(TL::THREADS);
+    if (causal) {
+        if (dropout) hipLaunchKernelGGL((dkdv16_kernel<T, D, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((dkdv16_kernel<T, D, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (dropout) hipLaunchKernelGGL((dkdv16_kernel<T, D, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((dkdv16_kernel<T, D, false, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
+                             hipStream_t stream) {
+    switch (e) {
+    case Elem::BF16:
+        return d == 64 ? launch_dkdv16_t<bf16, 64>(causal, dropout, a, stream)
+                       : launch_dkdv16_t<bf16, 128>(causal, dropout, a, stream);
+    case Elem::F16:
+        return d == 64 ? launch_dkdv16_t<f16, 64>(causal, dropout, a, stream)
+                       : launch_dkdv16_t<f16, 128>(causal, dropout, a, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa

@@ -25,7 +25,8 @@ struct BwdArgs {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
     void *dq, *dk, *dv;
-    float *dvec;          // workspace: D_i = dO_i . O_i, [B,H,N]
+    float *dvec;          // workspace: D_i / c, D_i = dO_i . O_i, [B,H,N]
+    float *nl2;           // workspace: -lse_i log2(e), [B,H,N]
     int64_t B, H, N;
     float scale;          // softmax scale
     float scale_log2;     // scale * log2(e)

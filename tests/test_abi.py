@@ -103,7 +103,7 @@ def test_workspace_size_and_too_small_workspace(lib):
     p = _p(B=2, H=3, N=100, d=128)
     rows = 2 * 3 * 100
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
-    assert need == (rows * 4 + 255) // 256 * 256
+    assert need == 2 * ((rows * 4 + 255) // 256 * 256)
     args = [FAKE] * 10
     assert lib.fa_bwd(ctypes.byref(p), *args, need - 1, None) == fa.FA_EINVAL
     assert "workspace" in lib.fa_last_error().decode()
@@ -126,8 +126,10 @@ def test_status_strings(lib):
 def test_backward_stages_validate(lib):
     p = _p(B=1, H=1, N=32, d=64)
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
-    assert lib.fa_bwd_prepare(ctypes.byref(p), FAKE, None, FAKE, need, None) == fa.FA_EINVAL
-    assert lib.fa_bwd_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, need - 4, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_prepare(ctypes.byref(p), FAKE, FAKE, None, FAKE, need, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_prepare(ctypes.byref(p), FAKE, None, FAKE, FAKE, need, None) == fa.FA_EINVAL
+    assert "lse" in lib.fa_last_error().decode()
+    assert lib.fa_bwd_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, need - 4, None) == fa.FA_EINVAL
     assert lib.fa_bwd_dkdv(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                            MISALIGNED, FAKE, need, None) == fa.FA_EINVAL
     assert "dv" in lib.fa_last_error().decode()
