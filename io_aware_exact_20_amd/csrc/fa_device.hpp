@@ -115,25 +115,29 @@ __device__ __forceinline__ float sum_halves(float x) {
 // round, with the key advanced by two Weyl increments between rounds.
 struct Philox4 { uint32_t x[4]; };
 
+constexpr uint32_t kPhiloxWeylA = 0x9E3779B9u, kPhiloxWeylB = 0xBB67AE85u;
+
+// Round r (0-based) of the generator on counter c under key (k0, k1): the
+// round key is the key advanced r times by the Weyl increments.
+__device__ __forceinline__ void philox_round(Philox4 &c, int r, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+    // One 32x32->64-bit product per word pair (v_mad_u64_u32 gives both
+    // halves in a single instruction).
+    const uint64_t pA = (uint64_t)kMulA * c.x[0], pB = (uint64_t)kMulB * c.x[2];
+    const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
+    const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
+    const uint32_t n0 = hiB ^ c.x[1] ^ (k0 + (uint32_t)r * kPhiloxWeylA);
+    const uint32_t n2 = hiA ^ c.x[3] ^ (k1 + (uint32_t)r * kPhiloxWeylB);
+    c.x[0] = n0; c.x[1] = loB; c.x[2] = n2; c.x[3] = loA;
+}
+
 __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
-    constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
-    constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+    Philox4 c;
+    c.x[0] = c0; c.x[1] = c1; c.x[2] = c2; c.x[3] = c3;
 #pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        // One 32x32->64-bit product per word pair (v_mad_u64_u32 gives both
-        // halves in a single instruction).
-        const uint64_t pA = (uint64_t)kMulA * c0, pB = (uint64_t)kMulB * c2;
-        const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
-        const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
-        const uint32_t n0 = hiB ^ c1 ^ k0;
-        const uint32_t n2 = hiA ^ c3 ^ k1;
-        c0 = n0; c1 = loB; c2 = n2; c3 = loA;
-        k0 += kWeylA; k1 += kWeylB;
-    }
-    Philox4 out;
-    out.x[0] = c0; out.x[1] = c1; out.x[2] = c2; out.x[3] = c3;
-    return out;
+    for (int r = 0; r < 10; ++r) philox_round(c, r, k0, k1);
+    return c;
 }
 
 // Keep bits of the eight columns 8*grp .. 8*grp+7 of one row: bit e is set

@@ -200,21 +200,51 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 
     // Keep masks of key block kb of this pair for tile t: lane (row lq,
     // half g) draws the 16 keys 32kb + 16g .. +15 of its row (two Philox
-    // blocks) and stores them as 16-bit masks.
-    auto gen_masks = [&](int t, int kb, int slot) {
+    // blocks) and stores them as 16-bit masks.  The draw is staged (counters,
+    // then the 20 block-rounds in order, then the masks) so that its rounds
+    // can be spread over the product groups of a step.
+    struct MaskDraw { Philox4 c[2]; };
+    auto mask_begin = [&](MaskDraw &m, int t, int kb) {
         const uint32_t grp = (uint32_t)((kp0 + 32 * kb) >> 3) + 2 * g;
         const uint32_t row = (uint32_t)((j0 + t) * BQ + lq);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            m.c[h].x[0] = grp + h;
+            m.c[h].x[1] = row;
+            m.c[h].x[2] = h_idx;
+            m.c[h].x[3] = b_idx;
+        }
+    };
+    // Block-rounds u0 .. u1-1 of 20: unit u is round u/2 of block u%2.  The
+    // state is pinned afterwards so that the rounds stay in the group that
+    // issues them.
+    auto mask_rounds = [&](MaskDraw &m, int u0, int u1) {
+#pragma unroll
+        for (int u = u0; u < u1; ++u) philox_round(m.c[u & 1], u >> 1, a.seed_lo, a.seed_hi);
+        if (u1 > u0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pin_vgpr(m.c[h].x[q]);
+        }
+    };
+    auto mask_end = [&](MaskDraw &m, int kb, int slot) {
         FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + (32 * kb + 16 * g) * 2;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const Philox4 r = philox4x32_10(grp + h, row, h_idx, b_idx, a.seed_lo, a.seed_hi);
             u32x4 w;
 #pragma unroll
             for (int q = 0; q < 4; ++q)   // word q: keys 2q (low half), 2q + 1 (high half)
-                w[q] = ((r.x[q] & 0xFFFFu) >= a.drop_T ? 0x0000FFFFu : 0u) |
-                       ((r.x[q] >> 16) >= a.drop_T ? 0xFFFF0000u : 0u);
+                w[q] = ((m.c[h].x[q] & 0xFFFFu) >= a.drop_T ? 0x0000FFFFu : 0u) |
+                       ((m.c[h].x[q] >> 16) >= a.drop_T ? 0xFFFF0000u : 0u);
             *(FA_LDS u32x4 *)(p + 16 * h) = w;
         }
+    };
+    auto gen_masks = [&](int t, int kb, int slot) {
+        MaskDraw m;
+        mask_begin(m, t, kb);
+        mask_rounds(m, 0, 20);
+        mask_end(m, kb, slot);
     };
     // Per-lane byte offset of the transposed mask read: lane receives the
     // masks of rows 8 q4 + 4g + 0..3 (its registers 4 q4 .. 4 q4 + 3) of key
@@ -339,11 +369,20 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 mma(sn[1], qf[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // ---- phase 2: dV^T += dO^T (keep P) of tile s.
+            // ---- phase 2: dV^T += dO^T (keep P) of tile s | keep masks of
+            // tile s+1 (block-rounds, cumulative count before group j: UA[j]).
+            constexpr int UA[9] = {0, 1, 2, 5, 8, 11, 14, 17, 20};
+            constexpr int UA64[5] = {0, 5, 10, 15, 20};
+            MaskDraw md;
+            if (DROPOUT) mask_begin(md, s + 1, 0);
 #pragma unroll
             for (int j = 0; j < 2 * NDB; ++j) {
                 const int cc = j / NDB, db = j % NDB;
                 if (j + 2 < 2 * NDB) of[(j + 2) % 3] = ofrag(j + 2);
+                if (DROPOUT) {
+                    if (NDB == 4) mask_rounds(md, UA[j], UA[j + 1]);
+                    else mask_rounds(md, UA64[j], UA64[j + 1]);
+                }
                 if (NDC == 8) {
                     if (j == 0) pgroup(0, 3);
                     if (j == 1) pgroup(1, 3);
@@ -362,7 +401,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (is_edge(s + 1)) apply_mask(sn, s + 1);
-            if (DROPOUT) gen_masks(s + 1, 0, R + 1);
+            if (DROPOUT) mask_end(md, 0, R + 1);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };
@@ -471,12 +510,21 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 mma(dcur[1], of[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // ---- phase 2: dK^T += Q^T dS of tile s-1.
+            // ---- phase 2: dK^T += Q^T dS of tile s-1 | keep masks of tile
+            // s+1 (block-rounds, cumulative count before group j: UB[j]).
+            constexpr int UB[9] = {0, 3, 6, 8, 11, 14, 16, 18, 20};
+            constexpr int UB64[5] = {0, 5, 10, 15, 20};
+            MaskDraw md;
+            if (DROPOUT) mask_begin(md, s + 1, 1);
             if (HP) {
 #pragma unroll
                 for (int j = 0; j < 2 * NDB; ++j) {
                     const int cc = j / NDB, db = j % NDB;
                     if (j + 2 < 2 * NDB) qt[(j + 2) % 3] = qfrag(j + 2);
+                    if (DROPOUT) {
+                        if (NDB == 4) mask_rounds(md, UB[j], UB[j + 1]);
+                        else mask_rounds(md, UB64[j], UB64[j + 1]);
+                    }
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
                         u32x4 p4;
@@ -489,7 +537,10 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            if (DROPOUT) gen_masks(s + 1, 1, R + 1);
+            if (DROPOUT) {
+                if (!HP) mask_rounds(md, 0, 20);
+                mask_end(md, 1, R + 1);
+            }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };

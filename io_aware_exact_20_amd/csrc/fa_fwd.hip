@@ -593,23 +593,17 @@ __global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a)
     __syncthreads();   // K buffer 0 is refilled in the first step
 
     // ---- steady state, two steps per trip (buffer parities are constants).
+    // The last step also forms S of tile Tw (never used: masked or
+    // zero-filled keys), so every step has one shape and the accumulators
+    // keep their registers across the loop exit.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using HN = std::true_type;
-    using NN = std::false_type;
-    int t = 0;
-    for (; t + 2 < Tw; t += 2) {
+    for (int t = 0; t < Tw; t += 2) {
         step(I0{}, HN{}, sA, sB, mx, t);
-        step(I1{}, HN{}, sB, sA, mx, t + 1);
+        if (t + 1 < Tw) step(I1{}, HN{}, sB, sA, mx, t + 1);
     }
-    if (t + 1 < Tw) {          // two tiles left
-        step(I0{}, HN{}, sA, sB, mx, t);
-        step(I1{}, NN{}, sB, sA, mx, t + 1);
-        t += 2;
-    } else if (t < Tw) {       // one tile left
-        step(I0{}, NN{}, sA, sB, mx, t);
-        t += 1;
-    }
+    int t = Tw > 0 ? Tw : 0;
     // Tiles beyond this wavefront's rows: keep the workgroup's loads and
     // barriers in step.
     for (; t < NT; ++t) {
