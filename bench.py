@@ -32,7 +32,10 @@ import workloads  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, causal, d=128) + % of MFMA peak"
-KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "bwd_dkdv": "fa_bwd.hip", "bwd_dq": "fa_bwd.hip"}
+# Sources of the 16-bit kernels each stage runs (the counters in
+# profiles/traffic.json are only used while these are unchanged).
+KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "bwd_dkdv": "fa_dkdv16.hip", "bwd_dq": "fa_bwd16.hip"}
+COPY_BYTES = 1 << 30             # the plain copy used to calibrate the HBM byte counters
 
 
 def log(msg):
@@ -42,7 +45,8 @@ def log(msg):
 def source_hash(name: str) -> str:
     path = os.path.join(ROOT, "io_aware_exact_20_amd", "csrc", name)
     h = hashlib.sha256()
-    for p in (path, os.path.join(ROOT, "io_aware_exact_20_amd", "csrc", "fa_device.hpp")):
+    for p in (path, os.path.join(ROOT, "io_aware_exact_20_amd", "csrc", "fa_device.hpp"),
+              os.path.join(ROOT, "io_aware_exact_20_amd", "csrc", "fa_kernels.hpp")):
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -126,6 +130,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of %d bytes three times (the "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)" % COPY_BYTES)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -135,9 +142,18 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    dev = "cuda:0"
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes three times" % COPY_BYTES)
+        return
+
     import io_aware_exact_20_amd as fa
     fa.load()
-    dev = "cuda:0"
     w = workloads.WORKLOADS["train_dropout"]
     F = w.flops_fwd()
     log("workload %s: B=%d H=%d N=%d d=%d causal p=%g" % (w.name, w.B, w.H, w.N, w.d, w.dropout_p))
