@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle baseline (0 disables it)")
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--profile-workload", default=None, metavar="NAME",
+                    help="only run --warmup + --steps steps of the named workload "
+                         "(%s) and log per-stage times; for profiler runs" % ", ".join(workloads.WORKLOADS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of %d bytes three times (the "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)" % COPY_BYTES)
@@ -154,6 +157,12 @@ def main():
 
     import io_aware_exact_20_amd as fa
     fa.load()
+    if args.profile_workload:
+        w = workloads.WORKLOADS[args.profile_workload]
+        prob = make_problem(fa, w, dev, with_bwd=w.backward)
+        wall, per = time_steps(prob, args.steps, args.warmup, with_bwd=w.backward)
+        log("workload %s: step %.3f ms; stages %s" % (w.name, wall, per))
+        return
     w = workloads.WORKLOADS["train_dropout"]
     F = w.flops_fwd()
     log("workload %s: B=%d H=%d N=%d d=%d causal p=%g" % (w.name, w.B, w.H, w.N, w.d, w.dropout_p))

@@ -126,8 +126,9 @@ __device__ __forceinline__ void philox_round(Philox4 &c, int r, uint32_t k0, uin
     const uint64_t pA = (uint64_t)kMulA * c.x[0], pB = (uint64_t)kMulB * c.x[2];
     const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
     const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
-    const uint32_t n0 = hiB ^ c.x[1] ^ (k0 + (uint32_t)r * kPhiloxWeylA);
-    const uint32_t n2 = hiA ^ c.x[3] ^ (k1 + (uint32_t)r * kPhiloxWeylB);
+    // Three-input XORs as single v_bitop3_b32 instructions (truth table 0x96).
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hiB, c.x[1], k0 + (uint32_t)r * kPhiloxWeylA, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hiA, c.x[3], k1 + (uint32_t)r * kPhiloxWeylB, 0x96);
     c.x[0] = n0; c.x[1] = loB; c.x[2] = n2; c.x[3] = loA;
 }
 
