@@ -260,7 +260,7 @@ struct Fwd16Tile {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <typename T, int D, int NW, bool CAUSAL, bool DROPOUT>
-__global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a) {
+__global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     using TL = Fwd16Tile<T, D, NW>;
     using SW = Swz<D>;
     constexpr int NB = TL::NB, BQ = TL::BQ, BC = TL::BC, RW = TL::RW;
@@ -320,15 +320,19 @@ __global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a)
                 voff[hf][db] = SW::off(8 * hf + 4 * (G >> 1) + k, 32 * db + 16 * (G & 1) + 4 * j);
     }
     // ---- direct tile loads: wave-instruction i of this wave fills tile rows
-    // R0 + i * RSTEP (R0 = first row of instruction 0 for this lane); the
-    // swizzled column of a lane does not depend on i.  Loads go through
-    // buffer resources bounded by the head's end, so the rows of the last
-    // tile past N arrive as zeros (masked scores, zero values).
+    // R0 + i * RSTEP (R0 = first row of instruction 0 for this lane).  The
+    // swizzle repeats every 16 rows, so the lane's swizzled column takes
+    // NPAT values over i.  Loads go through buffer resources bounded by the
+    // head's end, so the rows of the last tile past N arrive as zeros
+    // (masked scores, zero values).
     constexpr int RSTEP = NW * kWave / SW::CPR;
+    constexpr int NPAT = RSTEP % 16 == 0 ? 1 : 16 / RSTEP;
+    static_assert(16 % RSTEP == 0 || RSTEP % 16 == 0, "tile rows per load instruction");
     const int R0 = (wave * kWave + lane) / SW::CPR;
-    const uint32_t gcol = (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0)) * 8);
-    static_assert(RSTEP % 16 == 0, "the swizzle must repeat every RSTEP rows");
-    const uint32_t lane_boff = ((uint32_t)R0 * D + gcol) * 2;
+    uint32_t lane_boffs[NPAT];
+#pragma unroll
+    for (int i = 0; i < NPAT; ++i)
+        lane_boffs[i] = ((uint32_t)R0 * D + (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0 + i * RSTEP)) * 8)) * 2;
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
 
@@ -340,7 +344,7 @@ __global__ void __launch_bounds__(NW * 64, 4 / NW) fwd16_kernel(const FwdArgs a)
 
     // Load i of this wave's share of tile t of K (or V) into a buffer.
     auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf_lds, int i) {
-        buf2lds16(rs, lane_boff, (uint32_t)((t * BC + i * RSTEP) * D * 2),
+        buf2lds16(rs, lane_boffs[i % NPAT], (uint32_t)((t * BC + i * RSTEP) * D * 2),
                   buf_lds + (wave + i * NW) * (kWave * 16));
     };
     auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf_lds) {
