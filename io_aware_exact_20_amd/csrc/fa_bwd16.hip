@@ -169,11 +169,32 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         pin_vgpr(v);   // keeps the work in its group (no sinking)
         return v;
     };
-    auto keep_of = [&](int t, int nb) -> uint32_t {
-        if (!DROPOUT) return 0xFFFFu;
-        return keep_bits_row((uint32_t)(t * BC), (uint32_t)(q0w + 32 * nb + lq), h_idx, b_idx,
-                             a.seed_lo, a.seed_hi, a.drop_T);
+    // The keep bits of block nb of tile t (as keep_bits_row), drawn in stages:
+    // counters, then 20 block-rounds in order (unit u: round u/2 of block
+    // u%2), then the bits, so that the rounds can sit between the dQ
+    // products, which have no other VALU work.
+    struct KeepDraw { Philox4 c[2]; };
+    auto keep_begin = [&](KeepDraw &k, int t, int nb) {
+        const uint32_t grp = (uint32_t)((t * BC) >> 3) + 2 * (uint32_t)g;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            k.c[h].x[0] = grp + h;
+            k.c[h].x[1] = (uint32_t)(q0w + 32 * nb + lq);
+            k.c[h].x[2] = h_idx;
+            k.c[h].x[3] = b_idx;
+        }
     };
+    auto keep_rounds = [&](KeepDraw &k, int u0, int u1) {
+#pragma unroll
+        for (int u = u0; u < u1; ++u) philox_round(k.c[u & 1], u >> 1, a.seed_lo, a.seed_hi);
+        if (u1 > u0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pin_vgpr(k.c[h].x[q]);
+        }
+    };
+    auto keep_end = [&](KeepDraw &k) { return keep_bits_from_blocks(k.c[0], k.c[1], a.drop_T); };
 
     // Scores of the lane's blocks: `cur` = the block being produced, `prv`
     // = the block whose dS is being formed.
@@ -214,27 +235,36 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // 3x: dQ^T of block nb += K^T dS^T with K of slot sl.
-    auto phase3 = [&](auto nb_c, auto sl_c, const uint32_t (&dsv)[8]) {
+    // 3x: dQ^T of block nb += K^T dS^T with K of slot sl, one product per
+    // group with its K^T fragment read two groups ahead; the block-rounds of
+    // a keep draw (kd, if any) are spread over the groups.
+    auto phase3 = [&](auto nb_c, auto sl_c, const uint32_t (&dsv)[8], auto kd_c, KeepDraw &kd) {
         constexpr int NB_ = decltype(nb_c)::value, SL = decltype(sl_c)::value;
+        constexpr bool KD = decltype(kd_c)::value;
+        constexpr int NJ = 2 * NDB;
         const lds_char *kb = kbuf(SL);
+        auto ktfrag = [&](int j) {
+            const int cc = j / NDB, db = j % NDB;
+            const uint32_t kc_off = (uint32_t)(16 * cc * RB);
+            return join<T>(lds_half_tr<T>(kb + kc_off + toff[0][db]),
+                           lds_half_tr<T>(kb + kc_off + toff[1][db]));
+        };
+        frag_t<T> kt[3];
+        kt[0] = ktfrag(0);
+        kt[1] = ktfrag(1);
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int j = 0; j < NJ; ++j) {
+            const int cc = j / NDB, db = j % NDB;
+            if (j + 2 < NJ) kt[(j + 2) % 3] = ktfrag(j + 2);
+            if (DROPOUT && KD) keep_rounds(kd, (20 * j) / NJ, (20 * (j + 1)) / NJ);
             u32x4 pv;
             pv[0] = dsv[4 * cc + 0];
             pv[1] = dsv[4 * cc + 1];
             pv[2] = dsv[4 * cc + 2];
             pv[3] = dsv[4 * cc + 3];
-            const frag_t<T> sf = __builtin_bit_cast(frag_t<T>, pv);
-            const uint32_t kc_off = (uint32_t)(16 * cc * RB);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const frag_t<T> kt = join<T>(lds_half_tr<T>(kb + kc_off + toff[0][db]),
-                                             lds_half_tr<T>(kb + kc_off + toff[1][db]));
-                mma(dq[db][NB_], kt, sf);
-            }
+            mma(dq[db][NB_], kt[j % 3], __builtin_bit_cast(frag_t<T>, pv));
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
     };
 
     using I0 = std::integral_constant<int, 0>;
@@ -253,15 +283,19 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         // 1a: block a of tile t | dS of block b of tile t-1 | loads of tile t+1.
         phase1(I0{}, sl_c, hp_c, YES{}, s_a, dp_a, s_b, dp_b, keep_b, 1, dsb, t, sn_c);
         if (is_edge(t, 0)) apply_mask(s_a, t, 0);
-        if (DROPOUT) keep_a = keep_of(t, 0);
-        // 3b: dQ of block b with tile t-1.
-        if (HP) phase3(I1{}, sp_c, dsb);
+        // 3b: dQ of block b with tile t-1 | keep bits of block a of tile t.
+        KeepDraw kd;
+        if (DROPOUT) keep_begin(kd, t, 0);
+        if (HP) phase3(I1{}, sp_c, dsb, YES{}, kd);
+        else if (DROPOUT) keep_rounds(kd, 0, 20);
+        if (DROPOUT) keep_a = keep_end(kd);
         // 1b: block b of tile t | dS of block a of tile t.
         phase1(I1{}, sl_c, YES{}, NO{}, s_b, dp_b, s_a, dp_a, keep_a, 0, dsa, t, sn_c);
         if (is_edge(t, 1)) apply_mask(s_b, t, 1);
-        if (DROPOUT) keep_b = keep_of(t, 1);
-        // 3a: dQ of block a with tile t.
-        phase3(I0{}, sl_c, dsa);
+        // 3a: dQ of block a with tile t | keep bits of block b of tile t.
+        if (DROPOUT) keep_begin(kd, t, 1);
+        phase3(I0{}, sl_c, dsa, YES{}, kd);
+        if (DROPOUT) keep_b = keep_end(kd);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile t+1 landed
         __syncthreads();                 // everyone's; slot of tile t-2 free
     };
@@ -289,9 +323,10 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) dsb[i] = ds_pair(s_b, dp_b, keep_b, 1, i);
         const int sl = (Tw - 1) % 3;
-        if (sl == 0) phase3(I1{}, I0{}, dsb);
-        else if (sl == 1) phase3(I1{}, I1{}, dsb);
-        else phase3(I1{}, I2{}, dsb);
+        KeepDraw none;
+        if (sl == 0) phase3(I1{}, I0{}, dsb, NO{}, none);
+        else if (sl == 1) phase3(I1{}, I1{}, dsb, NO{}, none);
+        else phase3(I1{}, I2{}, dsb, NO{}, none);
     }
     // Tiles beyond this wavefront's rows: keep the workgroup's loads and barriers in step.
     for (; t < NT; ++t) {
