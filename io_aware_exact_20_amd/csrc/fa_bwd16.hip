@@ -162,7 +162,11 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
             const int r = 2 * i + e;
             const float p = fast_exp2(fmaf(s[r], sl2, -lse2[nb]));
             float dpv = dp[r];
-            if (DROPOUT) dpv = ((keep >> r) & 1u) ? dpv : 0.f;
+            if (DROPOUT) {
+                // keep bit r sign-extended to a 32-bit mask: dP or +0.
+                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)keep, r, 1);
+                dpv = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, dpv) & m);
+            }
             ds[e] = p * (dpv - dvec[nb]);
         }
         uint32_t v = pack2<T>(ds[0], ds[1]);
