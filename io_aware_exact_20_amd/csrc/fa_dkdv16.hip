@@ -263,14 +263,6 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     using I3 = std::integral_constant<int, 3>;
     using YES = std::true_type;
     using NO = std::false_type;
-    auto dispatch4 = [&](int r, auto f) {
-        switch (r & 3) {
-        case 0: f(I0{}); break;
-        case 1: f(I1{}); break;
-        case 2: f(I2{}); break;
-        default: f(I3{}); break;
-        }
-    };
 
     // ---- prologue loads: Q_0, Q_1, dO_0, rows of tile 0.
 #pragma unroll

@@ -282,6 +282,20 @@ def test_forward_is_deterministic(gpu_lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_is_deterministic(gpu_lib, d):
+    """No atomics anywhere: two backward runs on the same inputs agree bit for
+    bit (a race between the wavefronts sharing LDS buffers would show here)."""
+    w = Workload("detb", 2, 4, 1000, d, "bf16", causal=True, dropout_p=0.1, backward=True,
+                 seed=11, dropout_seed=77)
+    log("case detb d=%d" % d)
+    q, k, v, do = workloads.draw(w)
+    r1 = run_bwd(gpu_lib, w, q, k, v, do)
+    r2 = run_bwd(gpu_lib, w, q, k, v, do)
+    for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), r1, r2):
+        assert torch.equal(x, y), "%s differs between two runs" % name
+
+
 # ------------------------------------------------------ bit-exact probes
 
 def test_dropout_mask_bit_exact_full_planes(gpu_lib):
