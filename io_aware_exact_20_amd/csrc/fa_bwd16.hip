@@ -93,8 +93,6 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         for (int c = 0; c < NDC; ++c) {
             qf[nb][c] = load_frag<T>(Qg + (size_t)r * D + 16 * c + 8 * g);
             df[nb][c] = load_frag<T>(dOg + (size_t)r * D + 16 * c + 8 * g);
-            pin_agpr(qf[nb][c]);
-            pin_agpr(df[nb][c]);
         }
         lse2[nb] = row < N ? a.lse[(size_t)bh * (size_t)N + row] * kLog2eB : __builtin_huge_valf();
         dvec[nb] = row < N ? a.dvec[(size_t)bh * (size_t)N + row] : 0.f;
@@ -310,6 +308,14 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         load_part(krs, 0, kbuf(0), i);
         load_part(vrs, 0, vbuf(0), i);
     }
+    // Q and dO into AGPRs once all loads are in flight (a pin waits for its load).
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) {
+            pin_agpr(qf[nb][c]);
+            pin_agpr(df[nb][c]);
+        }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 

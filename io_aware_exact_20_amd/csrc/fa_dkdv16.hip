@@ -123,10 +123,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             int key = kp0 + 32 * kb + lq;
             key = key < N ? key : N - 1;
 #pragma unroll
-            for (int c = 0; c < NDC; ++c) {
-                kv[kb][c] = load_frag<T>(src + (size_t)key * D + 16 * c + 8 * g);
-                pin_agpr(kv[kb][c]);
-            }
+            for (int c = 0; c < NDC; ++c) kv[kb][c] = load_frag<T>(src + (size_t)key * D + 16 * c + 8 * g);
         }
     }
 
@@ -273,6 +270,11 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     }
     if (role == 0) load_rows(0, (lds_char *)nl_s[0]);
     else load_rows(0, (lds_char *)dv_s[0]);
+    // K or V into AGPRs once all loads are in flight (a pin waits for its load).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) pin_agpr(kv[kb][c]);
     if (DROPOUT) gen_masks(0, role, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();

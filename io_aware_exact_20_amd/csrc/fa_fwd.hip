@@ -271,8 +271,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     constexpr float kNegInf = -__builtin_huge_valf();
     static_assert(BC == 32 && NB == 2, "the step schedule below assumes 32-key tiles, 2 row blocks");
 
-    // LDS: K buffers at [0, 2TB), V buffers at [2TB, 4TB).
-    __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], vs0[TB], vs1[TB];
+    // LDS: three K buffers (tile t in buffer t % 3) and two V buffers (t & 1).
+    __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], ks2[TB], vs0[TB], vs1[TB];
 
     const int lane = (int)lane_in_wave();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -300,10 +300,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
         int r = q0w + 32 * nb + lq;
         r = r < N ? r : N - 1;
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) {
-            qf[nb][c] = load_frag<T>(Q + (size_t)r * D + 16 * c + 8 * g);
-            pin_agpr(qf[nb][c]);
-        }
+        for (int c = 0; c < NDC; ++c) qf[nb][c] = load_frag<T>(Q + (size_t)r * D + 16 * c + 8 * g);
     }
 
     // ---- per-lane LDS read offsets (bytes, relative to a tile buffer).
@@ -351,7 +348,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) load_part(rs, t, buf_lds, i);
     };
-    auto kbuf = [&](int buf) { return buf ? (lds_char *)ks1 : (lds_char *)ks0; };
+    auto kbuf = [&](int buf) {
+        return buf == 0 ? (lds_char *)ks0 : buf == 1 ? (lds_char *)ks1 : (lds_char *)ks2;
+    };
     auto vbuf = [&](int buf) { return buf ? (lds_char *)vs1 : (lds_char *)vs0; };
 
     // A tile needs masking if it reaches past the sequence end or, causal,
@@ -436,10 +435,18 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     static_assert(SB == 8 || SB == 4, "group plan for d = 128 or 64");
     constexpr int PB = 12;                   // pairs computed in B
     uint32_t keep_cur[NB];
-    auto step = [&](auto par_c, auto hn_c, f32x16 (&sc)[NB], f32x16 (&sn)[NB], float (&mx)[NB], int t) {
-        constexpr int VB = decltype(par_c)::value, KN = VB ^ 1;
-        constexpr bool HN = decltype(hn_c)::value;
-        const lds_char *kbl = KN ? (lds_char *)ks1 : (lds_char *)ks0;
+    // kp: the first two K fragments of tile t+1, read during the previous
+    // step (K tiles are loaded three steps ahead, so tile t+1 is complete
+    // before step t begins and its buffer is not refilled before step t+1).
+    auto step = [&](auto kb_c, auto par_c, f32x16 (&sc)[NB], f32x16 (&sn)[NB], float (&mx)[NB],
+                    frag_t<T> (&kp)[2], int t) {
+        constexpr int KB = decltype(kb_c)::value;   // K buffer of tile t+1: (t+1) % 3
+        constexpr int VB = decltype(par_c)::value;  // V buffer of tile t: t & 1
+        constexpr bool HN = true;
+        const lds_char *kbl = KB == 0 ? (lds_char *)ks0 : KB == 1 ? (lds_char *)ks1 : (lds_char *)ks2;
+        constexpr int KQ = (KB + 1) % 3;            // K buffer of tile t+2
+        const lds_char *kql = KQ == 0 ? (lds_char *)ks0 : KQ == 1 ? (lds_char *)ks1 : (lds_char *)ks2;
+        constexpr int KL = (KB + 2) % 3;            // K buffer refilled with tile t+3: t % 3
         const lds_char *vbl = VB ? (lds_char *)vs1 : (lds_char *)vs0;
 
         maybe_rescale(mx);
@@ -500,20 +507,26 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
                 mxp[nb] = fmaxf(mxp[nb], fmaxf(sn[nb][2 * w], sn[nb][2 * w + 1]));
         };
 
-        // ---- B: S of tile t+1 | pairs 0..11 | K loads of tile t+2.
+        // ---- B: S of tile t+1 | pairs 0..11 | K loads of tile t+3.
         frag_t<T> kf[3], vf[3];
-        if (HN) { kf[0] = kfrag(0); kf[1] = kfrag(1); }
+        kf[0] = kp[0];
+        kf[1] = kp[1];
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
+            // Half-group 2j: product with row block 0, then its share of the
+            // PB pairs (spread over the 2 SB products in order).
             if (HN) {
                 if (j + 2 < SB) kf[(j + 2) % 3] = kfrag(j + 2);
                 mma(sn[0], kf[j % 3], qf[0][j]);
             }
-            // Pairs of this group: PB pairs spread over SB groups in order.
 #pragma unroll
-            for (int p = (j * PB) / SB; p < ((j + 1) * PB) / SB; ++p) pair(p);
+            for (int p = (2 * j * PB) / (2 * SB); p < ((2 * j + 1) * PB) / (2 * SB); ++p) pair(p);
+            __builtin_amdgcn_sched_barrier(0);
+            // Half-group 2j+1: row block 1.
             if (HN) mma(sn[1], kf[j % 3], qf[1][j]);
-            if (j < LOADS) load_part(krs, t + 2, kbuf(VB), j);
+#pragma unroll
+            for (int p = ((2 * j + 1) * PB) / (2 * SB); p < ((2 * j + 2) * PB) / (2 * SB); ++p) pair(p);
+            if (j < LOADS) load_part(krs, t + 3, kbuf(KL), j);
             if (j == SB - 2) vf[0] = vfrag(0);
             if (j == SB - 1) vf[1] = vfrag(1);
             __builtin_amdgcn_sched_barrier(0);
@@ -521,30 +534,33 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
         if (HN && is_edge(t + 1)) apply_mask(sn, t + 1);
 
         // ---- C: PV of tile t | pairs 12..15, row sums, maxima of t+1 | V loads of t+1.
-        constexpr int HALF = SC / 2;             // groups that use key chunk 0
+        // Work of half-group k (one product each, k = 0 .. 2 SC - 1): pairs
+        // 12..15 over the first SC halves (before chunk 1's products), the
+        // 16 row sums and the 8 maxima spread over all of them.
+        auto cwork = [&](int k) {
+            if (k < SC) {
+#pragma unroll
+                for (int p = PB + (k * 4) / SC; p < PB + ((k + 1) * 4) / SC; ++p) pair(p);
+            }
+#pragma unroll
+            for (int w = (k * 16) / (2 * SC); w < ((k + 1) * 16) / (2 * SC); ++w) rowsum(w);
+            if (HN) {
+#pragma unroll
+                for (int w = (k * 8) / (2 * SC); w < ((k + 1) * 8) / (2 * SC); ++w) maxpair(w);
+            }
+        };
 #pragma unroll
         for (int j = 0; j < SC; ++j) {
             if (j + 2 < SC) vf[(j + 2) % 3] = vfrag(j + 2);
             const int cc = j / NDB, db = j % NDB;
             mma(o[db][0], vf[j % 3], pfrag(0, cc));
-            if (j < HALF) {
-                // pairs 12..15 (chunk 1), sums 0..3
-#pragma unroll
-                for (int p = PB + (j * 4) / HALF; p < PB + ((j + 1) * 4) / HALF; ++p) pair(p);
-#pragma unroll
-                for (int w = (j * 4) / HALF; w < ((j + 1) * 4) / HALF; ++w) rowsum(w);
-            } else {
-                // sums 4..15
-                const int jj = j - HALF;
-#pragma unroll
-                for (int w = 4 + (jj * 12) / HALF; w < 4 + ((jj + 1) * 12) / HALF; ++w) rowsum(w);
-            }
-            if (HN) {
-#pragma unroll
-                for (int w = (j * 8) / SC; w < ((j + 1) * 8) / SC; ++w) maxpair(w);
-            }
+            cwork(2 * j);
+            __builtin_amdgcn_sched_barrier(0);
             mma(o[db][1], vf[j % 3], pfrag(1, cc));
-            if (j < LOADS) load_part(vrs, t + 1, vbuf(KN), j);
+            cwork(2 * j + 1);
+            if (j < LOADS) load_part(vrs, t + 1, vbuf(VB ^ 1), j);
+            if (j == SC - 2) kp[0] = lds_frag<T>(kql + koff[0]);
+            if (j == SC - 1) kp[1] = lds_frag<T>(kql + koff[1]);
             if (j == SC - 1) {
                 // Keep the row sums and maxima in this group (no sinking).
 #pragma unroll
@@ -563,16 +579,23 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
             for (int nb = 0; nb < NB; ++nb) mx[nb] = mxp[nb];
             if (DROPOUT) draw_keep(keep_cur, t + 1);
         }
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of K_{t+2}, V_{t+1} landed
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of K_{t+3}, V_{t+1} landed
         __syncthreads();                 // ... everyone's; buffers of K_{t+1}, V_t free
     };
 
-    // ---- prologue: K_0, K_1, V_0; S and maxima of tile 0.
+    // ---- prologue: K_0, K_1, K_2, V_0; S and maxima of tile 0.
     f32x16 sA[NB], sB[NB];
     float mx[NB];
+    frag_t<T> kp[2];
     load_tile(krs, 0, kbuf(0));
     load_tile(krs, 1, kbuf(1));
+    load_tile(krs, 2, kbuf(2));
     load_tile(vrs, 0, vbuf(0));
+    // Q into AGPRs once all loads are in flight (a pin waits for its load).
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) pin_agpr(qf[nb][c]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (Tw > 0) {
@@ -594,24 +617,30 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
         }
         if (DROPOUT) draw_keep(keep_cur, 0);
     }
+    kp[0] = lds_frag<T>((lds_char *)ks1 + koff[0]);
+    kp[1] = lds_frag<T>((lds_char *)ks1 + koff[1]);
     __syncthreads();   // K buffer 0 is refilled in the first step
 
-    // ---- steady state, two steps per trip (buffer parities are constants).
+    // ---- steady state, six steps per trip (buffer indices are constants).
     // The last step also forms S of tile Tw (never used: masked or
     // zero-filled keys), so every step has one shape and the accumulators
     // keep their registers across the loop exit.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using HN = std::true_type;
-    for (int t = 0; t < Tw; t += 2) {
-        step(I0{}, HN{}, sA, sB, mx, t);
-        if (t + 1 < Tw) step(I1{}, HN{}, sB, sA, mx, t + 1);
+    using I2 = std::integral_constant<int, 2>;
+    for (int t = 0; t < Tw; t += 6) {
+        step(I1{}, I0{}, sA, sB, mx, kp, t);
+        if (t + 1 < Tw) step(I2{}, I1{}, sB, sA, mx, kp, t + 1);
+        if (t + 2 < Tw) step(I0{}, I0{}, sA, sB, mx, kp, t + 2);
+        if (t + 3 < Tw) step(I1{}, I1{}, sB, sA, mx, kp, t + 3);
+        if (t + 4 < Tw) step(I2{}, I0{}, sA, sB, mx, kp, t + 4);
+        if (t + 5 < Tw) step(I0{}, I1{}, sB, sA, mx, kp, t + 5);
     }
     int t = Tw > 0 ? Tw : 0;
     // Tiles beyond this wavefront's rows: keep the workgroup's loads and
     // barriers in step.
     for (; t < NT; ++t) {
-        load_tile(krs, t + 2, kbuf(t & 1));
+        load_tile(krs, t + 3, kbuf(t % 3));
         load_tile(vrs, t + 1, vbuf((t + 1) & 1));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
