@@ -181,6 +181,22 @@ __device__ __forceinline__ uint32_t keep_bits_from_blocks(const Philox4 &b0, con
     return g ? (recv | (own << 8)) : (own | (recv << 8));
 }
 
+// Keep masks of the two 16-bit lanes of a generator word: 0xFFFF in each half
+// whose lane value is at least the threshold T, 0 elsewhere, for both halves
+// at once.  Flipping the top bits maps the unsigned order of the lanes onto
+// the signed one; then lane >= T exactly when the saturating 16-bit difference
+// (T' - 1) - lane' is negative (T', lane': flipped), and an arithmetic shift
+// spreads its sign over the half.  kc2 = keep_cmp_const(T), 1 <= T <= 65535.
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+__host__ __device__ constexpr uint32_t keep_cmp_const(uint32_t T) {
+    return (((T ^ 0x8000u) - 1u) & 0xFFFFu) * 0x00010001u;
+}
+__device__ __forceinline__ uint32_t keep_mask2(uint32_t w, uint32_t kc2) {
+    const i16x2 lane = __builtin_bit_cast(i16x2, w ^ 0x80008000u);
+    const i16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(i16x2, kc2), lane);
+    return __builtin_bit_cast(uint32_t, d >> (i16x2){15, 15});
+}
+
 // Keep bits of the sixteen keys one lane holds in a 32x32 accumulator that
 // has one query row per lane (register r <-> key kbase + 8(r/4) + 4g +
 // r%4, g = lane / 32): bit r of the result.  Each half-wavefront draws two

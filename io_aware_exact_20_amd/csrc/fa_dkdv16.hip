@@ -198,8 +198,10 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     // Keep masks of key block kb of this pair for tile t: lane (row lq,
     // half g) draws the 16 keys 32kb + 16g .. +15 of its row (two Philox
     // blocks) and stores them as 16-bit masks.  The draw is staged (counters,
-    // then the 20 block-rounds in order, then the masks) so that its rounds
-    // can be spread over the product groups of a step.
+    // then the 20 block-rounds in order, then the masks): the rounds of tile
+    // s+2 are spread over the second product phase of step s and its masks
+    // are formed and stored during the first phase of step s+1, so no part
+    // of the draw waits at the end of a step.
     struct MaskDraw { Philox4 c[2]; };
     auto mask_begin = [&](MaskDraw &m, int t, int kb) {
         const uint32_t grp = (uint32_t)((kp0 + 32 * kb) >> 3) + 2 * g;
@@ -225,24 +227,17 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 for (int q = 0; q < 4; ++q) pin_vgpr(m.c[h].x[q]);
         }
     };
-    auto mask_end = [&](MaskDraw &m, int kb, int slot) {
+    // Masks of block h of a finished draw: word q of the block holds keys 2q
+    // (low half) and 2q + 1 (high half).
+    const uint32_t kc2 = keep_cmp_const(a.drop_T);
+    auto mask_end_half = [&](MaskDraw &m, int kb, int slot, int h) {
         FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + (32 * kb + 16 * g) * 2;
+        u32x4 w;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            u32x4 w;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)   // word q: keys 2q (low half), 2q + 1 (high half)
-                w[q] = ((m.c[h].x[q] & 0xFFFFu) >= a.drop_T ? 0x0000FFFFu : 0u) |
-                       ((m.c[h].x[q] >> 16) >= a.drop_T ? 0xFFFF0000u : 0u);
-            *(FA_LDS u32x4 *)(p + 16 * h) = w;
-        }
+        for (int q = 0; q < 4; ++q) w[q] = keep_mask2(m.c[h].x[q], kc2);
+        *(FA_LDS u32x4 *)(p + 16 * h) = w;
     };
-    auto gen_masks = [&](int t, int kb, int slot) {
-        MaskDraw m;
-        mask_begin(m, t, kb);
-        mask_rounds(m, 0, 20);
-        mask_end(m, kb, slot);
-    };
+    MaskDraw pend;   // draw whose masks are stored in the first phase of the next step
     // Per-lane byte offset of the transposed mask read: lane receives the
     // masks of rows 8 q4 + 4g + 0..3 (its registers 4 q4 .. 4 q4 + 3) of key
     // 32 kb + lq, with q4 and kb added as immediates.
@@ -275,7 +270,15 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int c = 0; c < NDC; ++c) pin_agpr(kv[kb][c]);
-    if (DROPOUT) gen_masks(0, role, 0);
+    if (DROPOUT) {
+        MaskDraw m0;                     // tile 0: complete
+        mask_begin(m0, 0, role);
+        mask_rounds(m0, 0, 20);
+        mask_end_half(m0, role, 0, 0);
+        mask_end_half(m0, role, 0, 1);
+        mask_begin(pend, 1, role);       // tile 1: stored during step 0
+        mask_rounds(pend, 0, 20);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -360,15 +363,16 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     pgroup(1, c);
                     ppair(c);
                 }
+                if (DROPOUT && (c == 1 || c == 3)) mask_end_half(pend, 0, R + 1, c >> 1);
                 mma(sn[1], qf[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- phase 2: dV^T += dO^T (keep P) of tile s | keep masks of
-            // tile s+1 (block-rounds, cumulative count before group j: UA[j]).
+            // tile s+2 (block-rounds, cumulative count before group j: UA[j]).
             constexpr int UA[9] = {0, 1, 2, 5, 8, 11, 14, 17, 20};
             constexpr int UA64[5] = {0, 5, 10, 15, 20};
             MaskDraw md;
-            if (DROPOUT) mask_begin(md, s + 1, 0);
+            if (DROPOUT) mask_begin(md, s + 2, 0);
 #pragma unroll
             for (int j = 0; j < 2 * NDB; ++j) {
                 const int cc = j / NDB, db = j % NDB;
@@ -395,7 +399,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (is_edge(s + 1)) apply_mask(sn, s + 1);
-            if (DROPOUT) mask_end(md, 0, R + 1);
+            if (DROPOUT) pend = md;
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         };
@@ -501,15 +505,16 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int i = IPG * c; i < IPG * (c + 1); ++i) dsitem(i);
                 }
+                if (DROPOUT && (c == 1 || c == 3)) mask_end_half(pend, 1, R + 1, c >> 1);
                 mma(dcur[1], of[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- phase 2: dK^T += Q^T dS of tile s-1 | keep masks of tile
-            // s+1 (block-rounds, cumulative count before group j: UB[j]).
+            // s+2 (block-rounds, cumulative count before group j: UB[j]).
             constexpr int UB[9] = {0, 3, 6, 8, 11, 14, 16, 18, 20};
             constexpr int UB64[5] = {0, 5, 10, 15, 20};
             MaskDraw md;
-            if (DROPOUT) mask_begin(md, s + 1, 1);
+            if (DROPOUT) mask_begin(md, s + 2, 1);
             if (HP) {
 #pragma unroll
                 for (int j = 0; j < 2 * NDB; ++j) {
@@ -533,7 +538,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             }
             if (DROPOUT) {
                 if (!HP) mask_rounds(md, 0, 20);
-                mask_end(md, 1, R + 1);
+                pend = md;
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
