@@ -43,9 +43,11 @@ fa_status_t check_params(const fa_params_t *p, bool *empty) {
     if (p->N > 0x7fffffffLL) return fail(FA_EINVAL, "N=%lld exceeds 2^31-1", (long long)p->N);
     if (p->dtype != FA_F32 && p->dtype != FA_BF16 && p->dtype != FA_F16)
         return fail(FA_EUNSUPPORTED, "dtype %d is not supported", (int)p->dtype);
-    if (p->d != 64 && p->d != 128)
-        return fail(FA_EUNSUPPORTED, "head dimension d=%lld is not supported (64 or 128)",
+    if (p->d != 32 && p->d != 64 && p->d != 96 && p->d != 128 && p->d != 256)
+        return fail(FA_EUNSUPPORTED, "head dimension d=%lld is not supported (32, 64, 96, 128, 256)",
                     (long long)p->d);
+    if (p->d == 256 && p->dtype == FA_F32)
+        return fail(FA_EUNSUPPORTED, "head dimension 256 needs 16-bit inputs");
     if (p->causal != 0 && p->causal != 1) return fail(FA_EINVAL, "causal must be 0 or 1");
     if (!std::isfinite(p->scale) || !(p->scale > 0.f))
         return fail(FA_EINVAL, "scale must be finite and positive (got %g)", (double)p->scale);

@@ -267,7 +267,7 @@ struct DqTile {
     static constexpr int BC = 64;                // keys per LDS tile
     static constexpr int CH = 16 / sizeof(T);
     static constexpr int LD = D + CH;
-    static constexpr int MIN_WG_PER_CU = sizeof(T) == 4 ? 1 : 2;
+    static constexpr int MIN_WG_PER_CU = (sizeof(T) == 4 || D > 128) ? 1 : 2;
 };
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>
@@ -439,12 +439,28 @@ static hipError_t launch_dq_t(bool causal, bool dropout, const BwdArgs &a, hipSt
     return hipGetLastError();
 }
 
-#define FA_DISPATCH_ELEM_D(e, d, FN, ...)                                              \
-    switch (e) {                                                                       \
-    case Elem::BF16: return d == 64 ? FN<bf16, 64>(__VA_ARGS__) : FN<bf16, 128>(__VA_ARGS__); \
-    case Elem::F16: return d == 64 ? FN<f16, 64>(__VA_ARGS__) : FN<f16, 128>(__VA_ARGS__);    \
-    case Elem::F32: return d == 64 ? FN<float, 64>(__VA_ARGS__) : FN<float, 128>(__VA_ARGS__); \
-    }                                                                                  \
+// Head dimensions: 32, 64, 96, 128 for every type; 256 for 16-bit types.
+#define FA_DISPATCH_D(T, d, FN, ...)                   \
+    switch (d) {                                       \
+    case 32: return FN<T, 32>(__VA_ARGS__);            \
+    case 64: return FN<T, 64>(__VA_ARGS__);            \
+    case 96: return FN<T, 96>(__VA_ARGS__);            \
+    case 128: return FN<T, 128>(__VA_ARGS__);          \
+    }
+#define FA_DISPATCH_ELEM_D(e, d, FN, ...)                                  \
+    switch (e) {                                                           \
+    case Elem::BF16:                                                       \
+        if (d == 256) return FN<bf16, 256>(__VA_ARGS__);                   \
+        FA_DISPATCH_D(bf16, d, FN, __VA_ARGS__)                            \
+        break;                                                             \
+    case Elem::F16:                                                        \
+        if (d == 256) return FN<f16, 256>(__VA_ARGS__);                    \
+        FA_DISPATCH_D(f16, d, FN, __VA_ARGS__)                             \
+        break;                                                             \
+    case Elem::F32:                                                        \
+        FA_DISPATCH_D(float, d, FN, __VA_ARGS__)                           \
+        break;                                                             \
+    }                                                                      \
     return hipErrorInvalidValue;
 
 hipError_t launch_bwd_pre(Elem e, int d, const BwdArgs &a, hipStream_t stream) {
@@ -453,13 +469,13 @@ hipError_t launch_bwd_pre(Elem e, int d, const BwdArgs &a, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                            hipStream_t stream) {
-    if (e != Elem::F32) return launch_bwd_dkdv16(e, d, causal, dropout, a, stream);
+    if (e != Elem::F32 && (d == 64 || d == 128)) return launch_bwd_dkdv16(e, d, causal, dropout, a, stream);
     FA_DISPATCH_ELEM_D(e, d, launch_dkdv_t, causal, dropout, a, stream)
 }
 
 hipError_t launch_bwd_dq(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                          hipStream_t stream) {
-    if (e != Elem::F32) return launch_bwd_dq16(e, d, causal, dropout, a, stream);
+    if (e != Elem::F32 && (d == 64 || d == 128)) return launch_bwd_dq16(e, d, causal, dropout, a, stream);
     FA_DISPATCH_ELEM_D(e, d, launch_dq_t, causal, dropout, a, stream)
 }
 

@@ -42,7 +42,7 @@ struct FwdTile {
     static constexpr int BC = 64;                 // keys per LDS tile
     static constexpr int CH = 16 / sizeof(T);     // elements per 16-byte access
     static constexpr int LD = D + CH;             // K and V row pitch in LDS (elements)
-    static constexpr int MIN_WG_PER_CU = sizeof(T) == 4 ? 1 : 2;
+    static constexpr int MIN_WG_PER_CU = (sizeof(T) == 4 || D > 128) ? 1 : 2;
 };
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>
@@ -713,16 +713,35 @@ static hipError_t launch_fwd_t(bool causal, bool dropout, const FwdArgs &a, hipS
 
 hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                       hipStream_t stream) {
+    // d = 64 and 128 with 16-bit inputs take the 64-rows-per-wavefront
+    // kernel; every other case the generic one (32 rows per wavefront).
     switch (e) {
     case Elem::BF16:
-        return d == 64 ? launch_fwd16_t<bf16, 64, FA_FWD_NW>(causal, dropout, a, stream)
-                       : launch_fwd16_t<bf16, 128, FA_FWD_NW>(causal, dropout, a, stream);
+        switch (d) {
+        case 32: return launch_fwd_t<bf16, 32>(causal, dropout, a, stream);
+        case 64: return launch_fwd16_t<bf16, 64, FA_FWD_NW>(causal, dropout, a, stream);
+        case 96: return launch_fwd_t<bf16, 96>(causal, dropout, a, stream);
+        case 128: return launch_fwd16_t<bf16, 128, FA_FWD_NW>(causal, dropout, a, stream);
+        case 256: return launch_fwd_t<bf16, 256>(causal, dropout, a, stream);
+        }
+        break;
     case Elem::F16:
-        return d == 64 ? launch_fwd16_t<f16, 64, FA_FWD_NW>(causal, dropout, a, stream)
-                       : launch_fwd16_t<f16, 128, FA_FWD_NW>(causal, dropout, a, stream);
+        switch (d) {
+        case 32: return launch_fwd_t<f16, 32>(causal, dropout, a, stream);
+        case 64: return launch_fwd16_t<f16, 64, FA_FWD_NW>(causal, dropout, a, stream);
+        case 96: return launch_fwd_t<f16, 96>(causal, dropout, a, stream);
+        case 128: return launch_fwd16_t<f16, 128, FA_FWD_NW>(causal, dropout, a, stream);
+        case 256: return launch_fwd_t<f16, 256>(causal, dropout, a, stream);
+        }
+        break;
     case Elem::F32:
-        return d == 64 ? launch_fwd_t<float, 64>(causal, dropout, a, stream)
-                       : launch_fwd_t<float, 128>(causal, dropout, a, stream);
+        switch (d) {
+        case 32: return launch_fwd_t<float, 32>(causal, dropout, a, stream);
+        case 64: return launch_fwd_t<float, 64>(causal, dropout, a, stream);
+        case 96: return launch_fwd_t<float, 96>(causal, dropout, a, stream);
+        case 128: return launch_fwd_t<float, 128>(causal, dropout, a, stream);
+        }
+        break;
     }
     return hipErrorInvalidValue;
 }

@@ -53,8 +53,9 @@ def _fwd(lib, p, ptr=FAKE):
 
 BAD = [
     (dict(B=-1), fa.FA_EINVAL), (dict(H=-3), fa.FA_EINVAL), (dict(N=-1), fa.FA_EINVAL),
-    (dict(N=2**31), fa.FA_EINVAL), (dict(d=96), fa.FA_EUNSUPPORTED),
-    (dict(d=0), fa.FA_EUNSUPPORTED), (dict(dtype=7), fa.FA_EUNSUPPORTED),
+    (dict(N=2**31), fa.FA_EINVAL), (dict(d=80), fa.FA_EUNSUPPORTED),
+    (dict(d=0), fa.FA_EUNSUPPORTED), (dict(d=512), fa.FA_EUNSUPPORTED),
+    (dict(d=256, dtype=fa.F32), fa.FA_EUNSUPPORTED), (dict(dtype=7), fa.FA_EUNSUPPORTED),
     (dict(scale=0.0), fa.FA_EINVAL), (dict(scale=-1.0), fa.FA_EINVAL),
     (dict(scale=float("inf")), fa.FA_EINVAL), (dict(scale=float("nan")), fa.FA_EINVAL),
     (dict(dropout_p=1.0), fa.FA_EINVAL), (dict(dropout_p=-0.1), fa.FA_EINVAL),

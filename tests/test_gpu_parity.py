@@ -126,6 +126,29 @@ def test_small_fwd_bwd_full(gpu_lib, w):
             compare(name, got, exact, w.dtype)
 
 
+HEAD_DIMS = []
+for dt, dims in (("bf16", (32, 96, 256)), ("f16", (32, 96, 256)), ("f32", (32, 96))):
+    for d in dims:
+        for causal, p in ((False, 0.0), (True, 0.1)) if dt != "bf16" else \
+                ((False, 0.0), (False, 0.1), (True, 0.0), (True, 0.1)):
+            HEAD_DIMS.append(Workload("hd_%s_d%d_c%d_p%g" % (dt, d, causal, p), 1, 2, 300, d, dt,
+                                      causal=causal, dropout_p=p, backward=True,
+                                      seed=40 + d + causal, dropout_seed=0xD1CE + d))
+
+
+@pytest.mark.parametrize("w", HEAD_DIMS, ids=[w.name for w in HEAD_DIMS])
+def test_other_head_dims_fwd_bwd_full(gpu_lib, w):
+    """Head dimensions 32, 96 and 256 (generic kernels): every element of O,
+    LSE, dQ, dK, dV at N=300, masks, dropout, all input types (256: 16-bit)."""
+    log("case %s" % w.name)
+    q, k, v, do = workloads.draw(w)
+    edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
+    for name, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
+                             ("dK", dk, edk), ("dV", dv, edv)):
+        compare(name, got, exact, w.dtype)
+
+
 def test_single_head_f32_fwd_bwd(gpu_lib):
     """B=1,H=1,N=128,d=64 fp32 non-causal forward and backward: max-abs 1e-5."""
     w = workloads.WORKLOADS["single_head_f32"]
