@@ -219,6 +219,18 @@ def main():
         extras["mid_fwdbwd_tflops"] = round(3.5 * w3.flops_fwd() / (wall3 * 1e-3) / 1e12, 2)
         del p3
         torch.cuda.empty_cache()
+        # The training shape at the other head dimensions (generic kernels).
+        hd = {}
+        for d in (32, 96, 256):
+            wd = workloads.WORKLOADS["train_d%d" % d]
+            pd = make_problem(fa, wd, dev)
+            walld, perd = time_steps(pd, 3, 1)
+            Fd = wd.flops_fwd()
+            hd[str(d)] = {"fwd_tflops": round(Fd / (perd["fwd"] * 1e-3) / 1e12, 2),
+                          "fwdbwd_tflops": round(3.5 * Fd / (walld * 1e-3) / 1e12, 2)}
+            del pd
+            torch.cuda.empty_cache()
+        extras["head_dims"] = hd
         log("extras %s" % extras)
 
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
