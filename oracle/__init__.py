@@ -66,6 +66,9 @@ def _bind(lib):
     lib.oracle_fwd_rows.argtypes = [i64, i64, vp, vp, vp, dbl, i32, dbl, u64, i64, i64,
                                     vp, i64, vp, vp]
     lib.oracle_fwd_rows.restype = i32
+    lib.oracle_fwd_cross.argtypes = [i64, i64, i64, vp, vp, vp, dbl, i32, dbl, u64, i64, i64,
+                                     vp, vp]
+    lib.oracle_fwd_cross.restype = i32
     lib.oracle_probs.argtypes = [i64, i64, vp, vp, dbl, i32, dbl, u64, i64, i64, vp, vp]
     lib.oracle_probs.restype = i32
     lib.oracle_bwd_head.argtypes = [i64, i64, vp, vp, vp, vp, dbl, i32, dbl, u64, i64, i64,
@@ -130,11 +133,14 @@ def fwd(q, k, v, scale: float, causal: bool = False, dropout_p: float = 0.0,
     """O [B,H,N,d] and LSE [B,H,N] in float64.
 
     ``heads``: optional list of (b, h) pairs; only those heads are evaluated
-    (the others are left as NaN).
+    (the others are left as NaN).  ``k`` and ``v`` may have a different
+    sequence length Nk than ``q`` (see oracle_fwd_cross for the causal rule).
     """
     lib = _load()
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
+    if k.shape[2] != N:
+        return _fwd_cross(lib, q, k, v, scale, causal, dropout_p, seed, heads)
     o = np.full((B, H, N, d), np.nan)
     lse = np.full((B, H, N), np.nan)
     todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
@@ -145,6 +151,25 @@ def fwd(q, k, v, scale: float, causal: bool = False, dropout_p: float = 0.0,
                                    float(scale), int(bool(causal)), float(dropout_p),
                                    seed & (2**64 - 1), b, h, None, N, _ptr(ob), _ptr(lb)),
                "fwd")
+        o[b, h] = ob
+        lse[b, h] = lb
+    return o, lse
+
+
+def _fwd_cross(lib, q, k, v, scale, causal, dropout_p, seed, heads):
+    """fwd for Nq != Nk, one oracle_fwd_cross call per head."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    o = np.full((B, H, Nq, d), np.nan)
+    lse = np.full((B, H, Nq), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        ob = np.zeros((Nq, d))
+        lb = np.zeros(Nq)
+        qh, kh, vh = (np.ascontiguousarray(x[b, h]) for x in (q, k, v))
+        _check(lib.oracle_fwd_cross(Nq, Nk, d, _ptr(qh), _ptr(kh), _ptr(vh), float(scale),
+                                    int(bool(causal)), float(dropout_p), seed & (2**64 - 1),
+                                    b, h, _ptr(ob), _ptr(lb)), "fwd_cross")
         o[b, h] = ob
         lse[b, h] = lb
     return o, lse

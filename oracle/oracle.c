@@ -209,6 +209,68 @@ int oracle_fwd_rows(int64_t N, int64_t d, const double *q, const double *k, cons
     return bad ? ORACLE_EINVAL : ORACLE_OK;
 }
 
+/* ------------------------------------------ queries and keys of two lengths */
+
+/*
+ * Forward of one (b, h) head with Nq query rows and Nk keys: cross
+ * attention, or the last Nq positions of a sequence of Nk (decoding).  When
+ * causal, the last query is aligned with the last key: key j is visible to
+ * query i iff j <= i + (Nk - Nq), which is the square rule when Nq == Nk; a
+ * query with no visible key gets O = 0, LSE = -inf.  Dropout uses the same
+ * counters as the square case with the query's own row index i.
+ * q: [Nq, d]; k, v: [Nk, d]; o_out: [Nq, d]; lse_out: [Nq].
+ */
+int oracle_fwd_cross(int64_t Nq, int64_t Nk, int64_t d, const double *q, const double *k,
+                     const double *v, double scale, int causal, double p, uint64_t seed,
+                     int64_t b, int64_t h, double *o_out, double *lse_out)
+{
+    if (Nq < 0 || Nk < 0 || d <= 0 || !(p >= 0.0 && p < 1.0)) return ORACLE_EINVAL;
+    int bad = 0;
+    #pragma omp parallel
+    {
+        size_t n = (size_t)(Nk > 0 ? Nk : 1);
+        double *s = (double *)malloc(sizeof(double) * n);
+        double *prob = (double *)malloc(sizeof(double) * n);
+        double *pd = (double *)malloc(sizeof(double) * n);
+        if (!s || !prob || !pd) {
+            #pragma omp atomic write
+            bad = 1;
+        } else {
+            #pragma omp for schedule(dynamic, 4)
+            for (int64_t i = 0; i < Nq; ++i) {
+                const double *qi = q + i * d;
+                const int64_t last = causal ? i + (Nk - Nq) : Nk - 1;   /* last visible key */
+                /* scores and the row's log-sum-exp (max, then sum) */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < Nk; ++j) {
+                    if (j > last) { s[j] = -INFINITY; continue; }
+                    double acc = 0.0;
+                    for (int64_t c = 0; c < d; ++c) acc += qi[c] * k[j * d + c];
+                    s[j] = acc * scale;
+                    if (s[j] > m) m = s[j];
+                }
+                double lse = -INFINITY;
+                if (m != -INFINITY) {
+                    double l = 0.0;
+                    for (int64_t j = 0; j < Nk; ++j)
+                        if (s[j] != -INFINITY) l += exp(s[j] - m);
+                    lse = m + log(l);
+                }
+                lse_out[i] = lse;
+                prob_row(Nk, s, lse, p, seed, b, h, i, prob, pd);
+                double *oi = o_out + i * d;
+                for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+                for (int64_t j = 0; j < Nk; ++j) {
+                    if (pd[j] == 0.0) continue;
+                    for (int64_t c = 0; c < d; ++c) oi[c] += pd[j] * v[j * d + c];
+                }
+            }
+        }
+        free(s); free(prob); free(pd);
+    }
+    return bad ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
 /* Probability rows of one head: prob, pd: [N, N]. */
 int oracle_probs(int64_t N, int64_t d, const double *q, const double *k, double scale,
                  int causal, double p, uint64_t seed, int64_t b, int64_t h,

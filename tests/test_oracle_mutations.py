@@ -41,6 +41,15 @@ MUTANTS = [
     ("value_row_index_swapped", "for (int64_t c = 0; c < d; ++c) oi[c] += pd[j] * vj[c];",
      "for (int64_t c = 0; c < d; ++c) oi[c] += pd[j] * v[i * d + c];",
      [lambda: pins.test_one_hot_values_select_probabilities(False, 0.0)]),
+    ("cross_causal_offset_sign", "const int64_t last = causal ? i + (Nk - Nq) : Nk - 1;",
+     "const int64_t last = causal ? i - (Nk - Nq) : Nk - 1;",
+     [lambda: pins.test_cross_causal_is_the_tail_of_the_square_problem(1, 40)]),
+    ("cross_last_key_dropped", "const int64_t last = causal ? i + (Nk - Nq) : Nk - 1;",
+     "const int64_t last = causal ? i + (Nk - Nq) : Nk - 2;",
+     [lambda: pins.test_cross_matches_torch_cpu_fp64_sdpa(5, 23, False)]),
+    ("cross_dropout_row_shifted", "prob_row(Nk, s, lse, p, seed, b, h, i, prob, pd);",
+     "prob_row(Nk, s, lse, p, seed, b, h, i + (Nk - Nq), prob, pd);",
+     [pins.test_cross_dropout_uses_the_square_counters]),
 ]
 
 

@@ -360,3 +360,82 @@ def test_mask_uses_eight_lanes_of_one_block():
             lanes += [int(w) & 0xFFFF, int(w) >> 16]
         expect = [int(x >= T) for x in lanes]
         assert list(m[row, 8 * c:8 * c + 8]) == expect
+
+
+# ------------------------------------------- queries and keys of two lengths
+
+def _cross_mask(Nq, Nk, causal):
+    """Visible (i, j): every key, or (causal) j <= i + (Nk - Nq)."""
+    if not causal:
+        return np.ones((Nq, Nk), dtype=bool)
+    return np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 9), (5, 23), (23, 5), (16, 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_cross_matches_torch_cpu_fp64_sdpa(Nq, Nk, causal):
+    """Nq != Nk: torch's fp64 scaled_dot_product_attention with the same
+    visibility as an explicit mask (rows with no visible key are compared
+    through the closed form O = 0, LSE = -inf instead)."""
+    d, scale = 6, 0.45
+    q, k, v = _rand((1, 2, Nq, d), 50), _rand((1, 2, Nk, d), 51), _rand((1, 2, Nk, d), 52)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    m = _cross_mask(Nq, Nk, causal)
+    live = m.any(axis=1)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=torch.from_numpy(m), scale=scale).numpy()
+    s = scale * np.einsum("bhid,bhjd->bhij", q, k)
+    s = np.where(m, s, -np.inf)
+    with np.errstate(divide="ignore"):
+        ref_lse = scipy.special.logsumexp(s, axis=-1)
+    np.testing.assert_allclose(o[:, :, live], ref[:, :, live], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse[:, :, live], ref_lse[:, :, live], rtol=1e-12, atol=1e-13)
+    assert np.all(o[:, :, ~live] == 0.0) and np.all(lse[:, :, ~live] == -np.inf)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 40), (7, 40), (40, 40)])
+def test_cross_causal_is_the_tail_of_the_square_problem(Nq, Nk):
+    """Causal with the last query aligned to the last key: the Nq queries
+    see exactly what the last Nq rows of the square problem over the Nk
+    keys see (decoding), so their O and LSE are those rows."""
+    d, scale = 5, 0.6
+    qf = _rand((1, 1, Nk, d), 60)
+    k, v = _rand((1, 1, Nk, d), 61), _rand((1, 1, Nk, d), 62)
+    o_sq, l_sq = oracle.fwd(qf, k, v, scale, True)
+    o, lse = oracle.fwd(np.ascontiguousarray(qf[:, :, Nk - Nq:]), k, v, scale, True)
+    np.testing.assert_allclose(o, o_sq[:, :, Nk - Nq:], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, l_sq[:, :, Nk - Nq:], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(9, 30), (30, 9)])
+def test_cross_zero_query_gives_mean_of_visible_values(Nq, Nk):
+    """Q = 0, causal: O_i is the mean of V_0 .. V_{i + Nk - Nq} and LSE_i the
+    log of their count; queries with no visible key give O = 0, LSE = -inf."""
+    d = 4
+    q = np.zeros((1, 1, Nq, d))
+    k, v = _rand((1, 1, Nk, d), 63), _rand((1, 1, Nk, d), 64)
+    o, lse = oracle.fwd(q, k, v, 0.5, True)
+    for i in range(Nq):
+        n = i + 1 + Nk - Nq
+        if n <= 0:
+            assert np.all(o[0, 0, i] == 0.0) and lse[0, 0, i] == -np.inf
+        else:
+            np.testing.assert_allclose(o[0, 0, i], v[0, 0, :n].mean(axis=0), rtol=0, atol=1e-13)
+            assert abs(lse[0, 0, i] - math.log(n)) < 1e-13
+
+
+def test_cross_dropout_uses_the_square_counters():
+    """With dropout, entry (i, j) of an Nq x Nk problem is kept iff entry
+    (i, j) of the plane's keep mask is: one-hot V (d >= Nk) exposes the
+    dropped, rescaled probabilities, which must be the undropped ones times
+    mask times c."""
+    Nq, Nk, d, p, seed = 6, 11, 12, 0.4, 0xABCDEF
+    q, k = _rand((1, 1, Nq, d), 65), _rand((1, 1, Nk, d), 66)
+    v = np.zeros((1, 1, Nk, d))
+    v[0, 0, :, :Nk] = np.eye(Nk)
+    pd, _ = oracle.fwd(q, k, v, 0.8, True, p, seed)
+    prob, _ = oracle.fwd(q, k, v, 0.8, True, 0.0, seed)
+    keep = oracle.dropout_mask(max(Nq, Nk), p, seed, 0, 0)[:Nq, :Nk]
+    c = oracle.keep_scale(p)
+    np.testing.assert_allclose(pd[0, 0, :, :Nk], prob[0, 0, :, :Nk] * keep * c, rtol=0, atol=1e-15)
