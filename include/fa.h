@@ -82,6 +82,16 @@ typedef enum fa_dtype {
  *                word w; kept iff lane >= round(p * 65536).
  *   seed       : dropout seed (ignored when dropout_p == 0).
  *   out_f32    : 0 -> outputs (o, dq, dk, dv) in `dtype`; 1 -> float32.
+ *   Nk         : keys (and values) per head for the forward; 0 means N
+ *                (self-attention).  With Nk != N the queries are the last N
+ *                positions of a sequence of Nk keys (decoding) or attend to
+ *                another sequence (cross attention): when causal, key j is
+ *                visible to query i iff j <= i + (Nk - N), so the last query
+ *                sees every key; a query with no visible key gets O = 0 and
+ *                LSE = -inf.  Dropout counters use the query's own row i.
+ *                The backward entry points need Nk == N (else
+ *                FA_EUNSUPPORTED).  One head of q, k or v must stay below
+ *                4 GiB (else FA_EUNSUPPORTED).
  */
 typedef struct fa_params {
     int64_t B, H, N, d;
@@ -91,16 +101,38 @@ typedef struct fa_params {
     float dropout_p;
     uint64_t seed;
     int32_t out_f32;
-    int32_t reserved;     /* must be 0 */
+    int32_t Nk;           /* keys per head; 0 = N */
 } fa_params_t;
 
 /*
- * Forward.  Reads q, k, v [B,H,N,d]; writes o [B,H,N,d] (dtype, or float32
- * with out_f32) and lse [B,H,N] float32 with lse_i = ln sum_j exp(s_ij) over
- * the visible keys of row i.  Nothing else is written to device memory.
+ * Forward.  Reads q [B,H,N,d] and k, v [B,H,Nk,d]; writes o [B,H,N,d]
+ * (dtype, or float32 with out_f32) and lse [B,H,N] float32 with
+ * lse_i = ln sum_j exp(s_ij) over the visible keys of row i.  Nothing else
+ * is written to device memory.
  */
 fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const void *v,
                    void *o, float *lse, void *stream);
+
+/*
+ * Forward with the keys of every (b, h, block of query rows) split into up
+ * to num_splits contiguous chunks (of a multiple of 64 keys) processed by
+ * separate workgroups, for problems with few query rows (decoding, short
+ * queries over long keys) that would otherwise leave most of the GPU idle:
+ * the sequence-length parallelism of the "FlashAttention-2" section of the
+ * interviewsvector.com page, applied to the keys.  Each chunk writes its O,
+ * normalised over its own keys, and its log-sum-exp to `workspace` (fp32);
+ * a second kernel merges them per row with the online-softmax rescaling
+ * (LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s).  Same
+ * arguments and results as fa_fwd (up to fp32 rounding order).
+ * 1 <= num_splits <= 256 (else FA_EINVAL).  `workspace` must hold
+ * fa_fwd_splitkv_workspace_bytes(p, num_splits) bytes (0 when fewer than
+ * two chunks result: then the plain forward runs and workspace may be
+ * NULL); its contents on entry are ignored.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(const fa_params_t *p, int32_t num_splits);
+fa_status_t fa_fwd_splitkv(const fa_params_t *p, const void *q, const void *k, const void *v,
+                           void *o, float *lse, int32_t num_splits, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of device workspace fa_bwd needs for `p` (0 for an empty problem,

@@ -38,7 +38,7 @@ class Params(ctypes.Structure):
                 ("d", ctypes.c_int64), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("dropout_p", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("out_f32", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("Nk", ctypes.c_int32)]
 
 
 assert ctypes.sizeof(Params) == 64
@@ -58,6 +58,10 @@ def load():
     vp, P, sz = ctypes.c_void_p, ctypes.POINTER(Params), ctypes.c_size_t
     lib.fa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
+    lib.fa_fwd_splitkv.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.argtypes = [P]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -85,12 +89,12 @@ def _check(status: int):
 
 
 def make_params(B, H, N, d, dtype=BF16, scale=None, causal=False, dropout_p=0.0, seed=0,
-                out_f32=False) -> Params:
+                out_f32=False, Nk=0) -> Params:
     return Params(B=B, H=H, N=N, d=d, dtype=dtype,
                   causal=int(bool(causal)),
                   scale=float(scale if scale is not None else 1.0 / math.sqrt(d)),
                   dropout_p=float(dropout_p), seed=int(seed) & (2**64 - 1),
-                  out_f32=int(bool(out_f32)), reserved=0)
+                  out_f32=int(bool(out_f32)), Nk=int(Nk))
 
 
 def _params_for(q: torch.Tensor, scale, causal, dropout_p, seed, out_f32) -> Params:
@@ -117,18 +121,48 @@ def _need(t, like, name):
                          (name, tuple(like.shape)))
 
 
-def fwd(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out_f32=False):
-    """Fused forward: returns (o [B,H,N,d], lse [B,H,N] float32)."""
-    lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, q, n)
-        if t.dtype != q.dtype:
-            raise ValueError("q, k, v must share a dtype")
+def _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32):
+    """Checks q [B,H,N,d] and k, v [B,H,Nk,d]; the params (Nk set when != N)."""
+    _need(q, q, "q")
+    _need(k, k, "k")
+    _need(v, k, "v")
+    if k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("k, v must be [B, H, Nk, d] with q's B, H, d")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
     p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
+    if k.shape[2] != q.shape[2]:
+        p.Nk = k.shape[2]
+    return p
+
+
+def fwd(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out_f32=False):
+    """Fused forward: returns (o [B,H,N,d], lse [B,H,N] float32); k and v
+    may hold Nk != N keys (see ``fa_params_t.Nk``)."""
+    lib = load()
+    p = _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32)
     o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                       _stream(q)))
+    return o, lse
+
+
+def fwd_splitkv(q, k, v, num_splits, scale=None, causal=False, dropout_p=0.0, seed=0,
+                out_f32=False, workspace=None):
+    """Forward with the keys split into up to ``num_splits`` chunks and
+    merged (``fa_fwd_splitkv``); same results as ``fwd``."""
+    lib = load()
+    p = _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32)
+    need = lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), int(num_splits))
+    if need == ctypes.c_size_t(-1).value:
+        raise FAError(FA_EINVAL, lib.fa_last_error().decode())
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(lib.fa_fwd_splitkv(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              int(num_splits), _ptr(workspace), workspace.numel(), _stream(q)))
     return o, lse
 
 

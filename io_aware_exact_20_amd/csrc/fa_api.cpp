@@ -54,7 +54,12 @@ fa_status_t check_params(const fa_params_t *p, bool *empty) {
     if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f))
         return fail(FA_EINVAL, "dropout_p must be in [0, 1) (got %g)", (double)p->dropout_p);
     if (p->out_f32 != 0 && p->out_f32 != 1) return fail(FA_EINVAL, "out_f32 must be 0 or 1");
-    if (p->reserved != 0) return fail(FA_EINVAL, "reserved field must be 0");
+    if (p->Nk < 0) return fail(FA_EINVAL, "Nk=%d is negative", (int)p->Nk);
+    // One head of any operand is addressed with 32-bit byte offsets.
+    const double head_bytes = (double)(p->Nk > p->N ? p->Nk : p->N) * (double)p->d *
+                              (p->dtype == FA_F32 || p->out_f32 ? 4.0 : 2.0);
+    if (head_bytes >= 4294967296.0)
+        return fail(FA_EUNSUPPORTED, "one head of %.3g bytes exceeds 4 GiB", head_bytes);
     // B*H*N*d must be addressable; the product of the extents is bounded
     // piecewise to avoid overflow in the check itself.
     const double total = (double)p->B * (double)p->H * (double)p->N * (double)p->d;
@@ -85,6 +90,51 @@ size_t row_array_bytes(const fa_params_t *p) {
 
 size_t workspace_bytes(const fa_params_t *p) { return 2 * row_array_bytes(p); }
 
+// Keys per head (Nk = 0 means N).
+int64_t keys(const fa_params_t *p) { return p->Nk ? (int64_t)p->Nk : p->N; }
+
+// A split forward: key chunks of a multiple of 64 keys; the number of
+// chunks actually used for `splits` requested.
+int64_t split_chunk(const fa_params_t *p, int32_t splits) {
+    const int64_t nk = keys(p);
+    const int64_t per = (nk + splits - 1) / splits;
+    return (per + 63) / 64 * 64;
+}
+int32_t splits_used(const fa_params_t *p, int32_t splits) {
+    const int64_t chunk = split_chunk(p, splits);
+    return (int32_t)((keys(p) + chunk - 1) / chunk);
+}
+constexpr int32_t kMaxSplits = 256;
+
+// The split workspace: the chunks' O (fp32, [S,B,H,N,d]) then their LSE
+// ([S,B,H,N]), each rounded up to 256 bytes.
+size_t split_o_bytes(const fa_params_t *p, int32_t splits) {
+    const size_t n = (size_t)splits * (size_t)p->B * (size_t)p->H * (size_t)p->N * (size_t)p->d;
+    return (n * 4 + 255) / 256 * 256;
+}
+size_t split_workspace_bytes(const fa_params_t *p, int32_t splits) {
+    return split_o_bytes(p, splits) + (size_t)splits * row_array_bytes(p);
+}
+
+// Forward argument block: one pass over all Nk keys (kv_splits = 1).
+fa::FwdArgs fwd_args(const fa_params_t *p, const void *q, const void *k, const void *v, void *o,
+                     float *lse) {
+    fa::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = p->B; a.H = p->H; a.N = p->N;
+    a.Nk = keys(p);
+    a.kv_splits = 1;
+    a.kv_chunk = (int32_t)((a.Nk + 63) / 64 * 64);
+    a.scale_log2 = p->scale * 1.44269504088896340736f;
+    const bool dropout = p->dropout_p > 0.f;
+    a.drop_T = dropout ? drop_threshold(p->dropout_p) : 0;
+    a.drop_c = dropout ? keep_scale(p->dropout_p) : 1.f;
+    a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
+    a.seed_hi = (uint32_t)(p->seed >> 32);
+    a.out_f32 = p->out_f32;
+    return a;
+}
+
 fa_status_t hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess)
         return fail(FA_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
@@ -104,24 +154,58 @@ fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const voi
     if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
         (s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")))
         return s;
-    fa::FwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = p->B; a.H = p->H; a.N = p->N;
-    a.scale_log2 = p->scale * 1.44269504088896340736f;
-    const bool dropout = p->dropout_p > 0.f;
-    a.drop_T = dropout ? drop_threshold(p->dropout_p) : 0;
-    a.drop_c = dropout ? keep_scale(p->dropout_p) : 1.f;
-    a.seed_lo = (uint32_t)(p->seed & 0xFFFFFFFFu);
-    a.seed_hi = (uint32_t)(p->seed >> 32);
-    a.out_f32 = p->out_f32;
-    return hip_status(fa::launch_fwd(elem(p->dtype), (int)p->d, p->causal != 0, dropout, a,
-                                     reinterpret_cast<hipStream_t>(stream)),
+    fa::FwdArgs a = fwd_args(p, q, k, v, o, lse);
+    return hip_status(fa::launch_fwd(elem(p->dtype), (int)p->d, p->causal != 0,
+                                     p->dropout_p > 0.f, a, reinterpret_cast<hipStream_t>(stream)),
                       "fa_fwd launch");
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(const fa_params_t *p, int32_t num_splits) {
+    bool empty = false;
+    if (check_params(p, &empty) != FA_OK) return (size_t)-1;
+    if (num_splits < 1 || num_splits > kMaxSplits) return (size_t)-1;
+    if (empty || splits_used(p, num_splits) < 2) return 0;
+    return split_workspace_bytes(p, num_splits);
+}
+
+fa_status_t fa_fwd_splitkv(const fa_params_t *p, const void *q, const void *k, const void *v,
+                           void *o, float *lse, int32_t num_splits, void *workspace,
+                           size_t workspace_size, void *stream) {
+    bool empty = false;
+    fa_status_t s = check_params(p, &empty);
+    if (s != FA_OK) return s;
+    if (num_splits < 1 || num_splits > kMaxSplits)
+        return fail(FA_EINVAL, "num_splits=%d outside 1..%d", (int)num_splits, (int)kMaxSplits);
+    if (empty) return ok();
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")))
+        return s;
+    fa::FwdArgs a = fwd_args(p, q, k, v, o, lse);
+    const int32_t used = splits_used(p, num_splits);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (used < 2)
+        return hip_status(fa::launch_fwd(elem(p->dtype), (int)p->d, p->causal != 0,
+                                         p->dropout_p > 0.f, a, st), "fa_fwd_splitkv launch");
+    if ((s = check_ptr(workspace, "workspace"))) return s;
+    const size_t need = split_workspace_bytes(p, num_splits);
+    if (workspace_size < need)
+        return fail(FA_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_size, need);
+    a.kv_splits = used;
+    a.kv_chunk = (int32_t)split_chunk(p, num_splits);
+    a.part_o = reinterpret_cast<float *>(workspace);
+    a.part_lse = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) +
+                                           split_o_bytes(p, num_splits));
+    s = hip_status(fa::launch_fwd(elem(p->dtype), (int)p->d, p->causal != 0,
+                                  p->dropout_p > 0.f, a, st), "fa_fwd_splitkv launch");
+    if (s != FA_OK) return s;
+    return hip_status(fa::launch_fwd_merge(elem(p->dtype), (int)p->d, a, st),
+                      "fa_fwd_splitkv merge launch");
 }
 
 size_t fa_bwd_workspace_bytes(const fa_params_t *p) {
     bool empty = false;
-    if (check_params(p, &empty) != FA_OK) return (size_t)-1;
+    if (check_params(p, &empty) != FA_OK || keys(p) != p->N) return (size_t)-1;
     if (empty) return 0;
     return workspace_bytes(p);
 }
@@ -135,7 +219,11 @@ namespace {
 fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t workspace_size,
                       bool *empty, fa::BwdArgs *a) {
     fa_status_t s = check_params(p, empty);
-    if (s != FA_OK || *empty) return s;
+    if (s != FA_OK) return s;
+    if (keys(p) != p->N)
+        return fail(FA_EUNSUPPORTED, "the backward needs as many keys as queries (Nk=%d, N=%lld)",
+                    (int)p->Nk, (long long)p->N);
+    if (*empty) return s;
     if ((s = check_ptr(workspace, "workspace"))) return s;
     const size_t need = workspace_bytes(p);
     if (workspace_size < need)

@@ -62,21 +62,28 @@ fwd_kernel(const FwdArgs a) {
     const int wave = tid / kWave, lane = tid % kWave;
     const int lq = lane % 32, g = lane / 32;
 
-    // Work unit: causal units are visited longest first.
+    // Work unit: (batch, head), query block, key chunk; causal query blocks
+    // longest first.
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
     const int64_t u = blockIdx.x;
     const int64_t bh = u % BH;
-    const int64_t qb = CAUSAL ? (nqb - 1 - u / BH) : (u / BH);
-    const int64_t N = a.N;
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const int64_t qi = (u / BH) / a.kv_splits;
+    const int split = (int)((u / BH) % a.kv_splits);
+    const int64_t qb = CAUSAL ? (nqb - 1 - qi) : qi;
+    const int64_t N = a.N, Nk = a.Nk;
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
     const T *__restrict__ Q = reinterpret_cast<const T *>(a.q) + head;
-    const T *__restrict__ K = reinterpret_cast<const T *>(a.k) + head;
-    const T *__restrict__ V = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ K = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ V = reinterpret_cast<const T *>(a.v) + head_kv;
     const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
 
     const int64_t q0 = qb * BQ;
     const int64_t qrow = q0 + wave * 32 + lq;   // this lane's query row
+    // Keys of this unit: [klo, khi); causal rows see keys up to row + off.
+    const int64_t klo = (int64_t)split * a.kv_chunk;
+    const int64_t khi = klo + a.kv_chunk < Nk ? klo + a.kv_chunk : Nk;
+    const int64_t off = Nk - N;
 
     // Q stays in registers for the whole key loop: B operand of S^T = K Q^T.
     frag_t<T> qf[NDC];
@@ -86,8 +93,9 @@ fwd_kernel(const FwdArgs a) {
         else qf[c] = frag_t<T>{};
     }
 
-    const int64_t kend = CAUSAL ? (q0 + BQ < N ? q0 + BQ : N) : N;
-    const int ntiles = (int)((kend + BC - 1) / BC);
+    int64_t kend = CAUSAL ? q0 + BQ + off : Nk;
+    kend = kend < khi ? kend : khi;
+    const int ntiles = kend > klo ? (int)((kend - klo + BC - 1) / BC) : 0;
 
     TileCopy<T, BC, D, THREADS> kcopy, vcopy;
 
@@ -97,8 +105,8 @@ fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-    kcopy.load(K, 0, N, tid);
-    vcopy.load(V, 0, N, tid);
+    kcopy.load(K, klo, Nk, tid);
+    vcopy.load(V, klo, Nk, tid);
     kcopy.template store<LD>(Ks[0], tid);
     vcopy.template store<LD>(Vs[0], tid);
     __syncthreads();
@@ -108,8 +116,8 @@ fwd_kernel(const FwdArgs a) {
         const T *ks = Ks[buf];
         const T *vs = Vs[buf];
         if (t + 1 < ntiles) {
-            kcopy.load(K, (int64_t)(t + 1) * BC, N, tid);
-            vcopy.load(V, (int64_t)(t + 1) * BC, N, tid);
+            kcopy.load(K, klo + (int64_t)(t + 1) * BC, Nk, tid);
+            vcopy.load(V, klo + (int64_t)(t + 1) * BC, Nk, tid);
         }
 
         // S^T for the tile's 32-key blocks.
@@ -124,16 +132,16 @@ fwd_kernel(const FwdArgs a) {
             }
         }
 
-        // Causal and sequence-end masking (only tiles that reach them).
-        const int64_t k0 = (int64_t)t * BC;
-        const bool edge = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+        // Causal and key-end masking (only tiles that reach them).
+        const int64_t k0 = klo + (int64_t)t * BC;
+        const bool edge = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0 + off);
         if (edge) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int64_t key = k0 + kb * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-                    if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = kNegInf;
+                    if (key >= Nk || (CAUSAL && key > qrow + off)) s[kb][r] = kNegInf;
                 }
         }
 
@@ -195,9 +203,13 @@ fwd_kernel(const FwdArgs a) {
         __syncthreads();
     }
 
-    // Epilogue: O = c * acc / l and LSE = ln(l) + max; rows past N are not stored.
+    // Epilogue: O = c * acc / l and LSE = ln(l) + max -- of the chunk, in
+    // fp32 to the partial buffers, when the keys are split; rows past N are
+    // not stored.
     const float l_tot = sum_halves(l_run);
     const float inv = l_tot > 0.f ? (DROPOUT ? a.drop_c : 1.f) / l_tot : 0.f;
+    const bool part = a.kv_splits > 1;
+    const size_t prow = ((size_t)split * (size_t)BH + (size_t)bh) * (size_t)N;
     if (qrow < N) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -206,7 +218,9 @@ fwd_kernel(const FwdArgs a) {
                 const int col = 32 * db + 8 * rr + 4 * g;
                 const float x0 = acc[db][4 * rr + 0] * inv, x1 = acc[db][4 * rr + 1] * inv;
                 const float x2 = acc[db][4 * rr + 2] * inv, x3 = acc[db][4 * rr + 3] * inv;
-                if (a.out_f32) {
+                if (part) {
+                    store4<float>(a.part_o + (prow + qrow) * D + col, x0, x1, x2, x3);
+                } else if (a.out_f32) {
                     float *O = reinterpret_cast<float *>(a.o) + head;
                     store4<float>(O + qrow * D + col, x0, x1, x2, x3);
                 } else {
@@ -217,7 +231,8 @@ fwd_kernel(const FwdArgs a) {
         if (g == 0) {
             const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f
                                           : kNegInf;
-            a.lse[(size_t)bh * (size_t)N + qrow] = lse;
+            if (part) a.part_lse[prow + qrow] = lse;
+            else a.lse[(size_t)bh * (size_t)N + qrow] = lse;
         }
     }
 }
@@ -278,20 +293,28 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lq = lane & 31, g = lane >> 5;
 
+    // Work unit: (batch, head), query block, key chunk; causal query blocks
+    // longest first.
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
     const int64_t u = blockIdx.x;
     const int64_t bh = u % BH;
-    const int64_t qb = CAUSAL ? (nqb - 1 - u / BH) : (u / BH);
-    const int N = (int)a.N;
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const int64_t qi = (u / BH) / a.kv_splits;
+    const int split = (int)((u / BH) % a.kv_splits);
+    const int64_t qb = CAUSAL ? (nqb - 1 - qi) : qi;
+    const int N = (int)a.N, Nk = (int)a.Nk;
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
     const T *__restrict__ Q = reinterpret_cast<const T *>(a.q) + head;
-    const T *__restrict__ K = reinterpret_cast<const T *>(a.k) + head;
-    const T *__restrict__ V = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ K = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ V = reinterpret_cast<const T *>(a.v) + head_kv;
     const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
 
     const int q0 = (int)qb * BQ;             // first query row of the workgroup
     const int q0w = q0 + wave * RW;           // first query row of this wavefront
+    // Keys of this unit: [klo, khi); causal rows see keys up to row + off.
+    const int klo = split * a.kv_chunk;
+    const int khi = (int)((int64_t)klo + a.kv_chunk < (int64_t)Nk ? klo + a.kv_chunk : Nk);
+    const int64_t off = (int64_t)Nk - N;
 
     // ---- Q fragments (B operand of S^T = K Q^T), rows clamped into range.
     frag_t<T> qf[NB][NDC];
@@ -330,18 +353,21 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < NPAT; ++i)
         lane_boffs[i] = ((uint32_t)R0 * D + (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0 + i * RSTEP)) * 8)) * 2;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const uint32_t head_bytes = (uint32_t)Nk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
 
-    const int kend = CAUSAL ? (q0 + BQ < N ? q0 + BQ : N) : N;
-    const int NT = (kend + BC - 1) / BC;                 // tiles the workgroup streams
-    // Tiles this wavefront needs (causal: up to its own last row).
-    const int wend = CAUSAL ? (q0w + RW < N ? q0w + RW : N) : N;
-    const int Tw = (wend + BC - 1) / BC;
+    // Tiles (of BC keys from klo) the workgroup streams, and the ones this
+    // wavefront needs (causal: up to its own last row).
+    auto tiles_to = [&](int64_t end) {
+        end = end < khi ? end : khi;
+        return end > klo ? (int)((end - klo + BC - 1) / BC) : 0;
+    };
+    const int NT = tiles_to(CAUSAL ? (int64_t)q0 + BQ + off : (int64_t)Nk);
+    const int Tw = tiles_to(CAUSAL ? (int64_t)q0w + RW + off : (int64_t)Nk);
 
     // Load i of this wave's share of tile t of K (or V) into a buffer.
     auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf_lds, int i) {
-        buf2lds16(rs, lane_boffs[i % NPAT], (uint32_t)((t * BC + i * RSTEP) * D * 2),
+        buf2lds16(rs, lane_boffs[i % NPAT], (uint32_t)((klo + t * BC + i * RSTEP) * D * 2),
                   buf_lds + (wave + i * NW) * (kWave * 16));
     };
     auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf_lds) {
@@ -353,22 +379,25 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     };
     auto vbuf = [&](int buf) { return buf ? (lds_char *)vs1 : (lds_char *)vs0; };
 
-    // A tile needs masking if it reaches past the sequence end or, causal,
-    // past this wavefront's first query row.
-    auto is_edge = [&](int t) { return (t * BC + BC > N) || (CAUSAL && t * BC + BC - 1 > q0w); };
+    // A tile needs masking if it reaches past the last key or, causal, past
+    // what this wavefront's first query row sees.
+    auto is_edge = [&](int t) {
+        const int64_t k0 = (int64_t)klo + t * BC;
+        return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + off);
+    };
     // Scores of tile t set to -inf where the key is masked for the query.
     auto apply_mask = [&](f32x16 (&s)[NB], int t) {
-        const int k0 = t * BC;
+        const int k0 = klo + t * BC;
         // Register r of block nb holds key k0 + 4g + kk(r) for query
-        // q0w + 32nb + lq, kk(r) = 8(r/4) + r%4.  Masked: key >= N, or
-        // (causal) key > query, i.e. kk(r) > lim[nb].
+        // q0w + 32nb + lq, kk(r) = 8(r/4) + r%4.  Masked: key >= Nk, or
+        // (causal) key > query + off, i.e. kk(r) > lim[nb].
         int lim[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            int l = N - 1 - (k0 + 4 * g);
+            int l = Nk - 1 - (k0 + 4 * g);
             if (CAUSAL) {
-                const int c = q0w + 32 * nb + lq - (k0 + 4 * g);
-                l = c < l ? c : l;
+                const int64_t c = (int64_t)q0w + 32 * nb + lq + off - (k0 + 4 * g);
+                l = c < l ? (int)(c > -64 ? c : -64) : l;
             }
             lim[nb] = l;
         }
@@ -397,7 +426,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     auto draw_keep = [&](uint32_t (&keep)[NB], int t) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-            keep[nb] = keep_bits_row((uint32_t)(t * BC), (uint32_t)(q0w + 32 * nb + lq), h_idx, b_idx,
+            keep[nb] = keep_bits_row((uint32_t)(klo + t * BC), (uint32_t)(q0w + 32 * nb + lq), h_idx, b_idx,
                                      a.seed_lo, a.seed_hi, a.drop_T);
     };
     // Move the reference maxima when a tile exceeds them by the threshold.
@@ -646,7 +675,10 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue: O = c * acc / l, LSE = (m + log2 l) ln 2.
+    // ---- epilogue: O = c * acc / l, LSE = (m + log2 l) ln 2 -- of the
+    // chunk, in fp32 to the partial buffers, when the keys are split.
+    const bool part = a.kv_splits > 1;
+    const size_t prow = ((size_t)split * (size_t)BH + (size_t)bh) * (size_t)N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int qrow = q0w + 32 * nb + lq;
@@ -660,7 +692,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
                     const int col = 32 * db + 8 * rr + 4 * g;
                     const float x0 = o[db][nb][4 * rr + 0] * inv, x1 = o[db][nb][4 * rr + 1] * inv;
                     const float x2 = o[db][nb][4 * rr + 2] * inv, x3 = o[db][nb][4 * rr + 3] * inv;
-                    if (a.out_f32) {
+                    if (part) {
+                        store4<float>(a.part_o + (prow + qrow) * D + col, x0, x1, x2, x3);
+                    } else if (a.out_f32) {
                         float *O = reinterpret_cast<float *>(a.o) + head;
                         store4<float>(O + (size_t)qrow * D + col, x0, x1, x2, x3);
                     } else {
@@ -671,7 +705,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
             if (g == 0) {
                 const float lse = l_tot > 0.f ? (m_run[nb] + __log2f(l_tot)) * 0.69314718055994530942f
                                               : kNegInf;
-                a.lse[(size_t)bh * (size_t)N + qrow] = lse;
+                if (part) a.part_lse[prow + qrow] = lse;
+                else a.lse[(size_t)bh * (size_t)N + qrow] = lse;
             }
         }
     }
@@ -681,7 +716,7 @@ template <typename T, int D, int NW>
 static hipError_t launch_fwd16_t(bool causal, bool dropout, const FwdArgs &a, hipStream_t stream) {
     using TL = Fwd16Tile<T, D, NW>;
     const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
-    const int64_t units = a.B * a.H * nqb;
+    const int64_t units = a.B * a.H * nqb * a.kv_splits;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
     if (causal) {
@@ -698,7 +733,7 @@ template <typename T, int D>
 static hipError_t launch_fwd_t(bool causal, bool dropout, const FwdArgs &a, hipStream_t stream) {
     constexpr int BQ = FwdTile<T, D>::BQ;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
-    const int64_t units = a.B * a.H * nqb;
+    const int64_t units = a.B * a.H * nqb * a.kv_splits;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(FwdTile<T, D>::THREADS);
     if (causal) {
@@ -709,6 +744,76 @@ static hipError_t launch_fwd_t(bool causal, bool dropout, const FwdArgs &a, hipS
         else hipLaunchKernelGGL((fwd_kernel<T, D, false, false>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
+}
+
+// ===================================================================
+// Merge of the key-chunk results of a split forward.  Chunk s holds, per
+// query row, O_s normalised over its own keys and LSE_s; the row's result is
+// LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s, the same
+// rescaling the online softmax applies between key tiles ("Tiling",
+// mrodiduger.github.io page).  A row that no chunk sees gets O = 0,
+// LSE = -inf.  One thread per four columns of a row.
+template <typename TO, int D>
+__global__ void __launch_bounds__(256) fwd_merge_kernel(const FwdArgs a, int64_t rows) {
+    constexpr int CPR = D / 4;
+    constexpr float kNegInf = -__builtin_huge_valf();
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = idx / CPR;
+    const int col = (int)(idx % CPR) * 4;
+    if (row >= rows) return;
+    const int S = a.kv_splits;
+    float m = kNegInf;
+    for (int s = 0; s < S; ++s) m = fmaxf(m, a.part_lse[(size_t)s * rows + row]);
+    float l = 0.f, x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f;
+    if (m != kNegInf) {
+        for (int s = 0; s < S; ++s) {
+            const float ls = a.part_lse[(size_t)s * rows + row];
+            const float w = ls == kNegInf ? 0.f : expf(ls - m);
+            const float4 x = *reinterpret_cast<const float4 *>(a.part_o + ((size_t)s * rows + row) * D + col);
+            l += w;
+            x0 = fmaf(w, x.x, x0);
+            x1 = fmaf(w, x.y, x1);
+            x2 = fmaf(w, x.z, x2);
+            x3 = fmaf(w, x.w, x3);
+        }
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    store4<TO>(reinterpret_cast<TO *>(a.o) + (size_t)row * D + col, x0 * inv, x1 * inv, x2 * inv, x3 * inv);
+    if (col == 0) a.lse[row] = l > 0.f ? m + logf(l) : kNegInf;
+}
+
+template <typename T, int D>
+static hipError_t launch_merge_t(const FwdArgs &a, hipStream_t stream) {
+    const int64_t rows = a.B * a.H * a.N;
+    const int64_t threads = rows * (D / 4);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (a.out_f32 || sizeof(T) == 4)
+        hipLaunchKernelGGL((fwd_merge_kernel<float, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a, rows);
+    else
+        hipLaunchKernelGGL((fwd_merge_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a, rows);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_merge_d(int d, const FwdArgs &a, hipStream_t stream) {
+    switch (d) {
+    case 32: return launch_merge_t<T, 32>(a, stream);
+    case 64: return launch_merge_t<T, 64>(a, stream);
+    case 96: return launch_merge_t<T, 96>(a, stream);
+    case 128: return launch_merge_t<T, 128>(a, stream);
+    case 256: return launch_merge_t<T, 256>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream) {
+    switch (e) {
+    case Elem::BF16: return launch_merge_d<bf16>(d, a, stream);
+    case Elem::F16: return launch_merge_d<f16>(d, a, stream);
+    case Elem::F32: return launch_merge_d<float>(d, a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,

@@ -14,6 +14,11 @@ struct FwdArgs {
     void *o;
     float *lse;
     int64_t B, H, N;
+    int64_t Nk;           // keys (and values) per head; queries see key j <= i + Nk - N when causal
+    int32_t kv_splits;    // key chunks per query block (1: one pass over all keys)
+    int32_t kv_chunk;     // keys per chunk, a multiple of 64
+    float *part_o;        // kv_splits > 1: O of each chunk [kv_splits,B,H,N,D] fp32, normalised
+    float *part_lse;      // kv_splits > 1: log-sum-exp of each chunk [kv_splits,B,H,N]
     float scale_log2;     // softmax scale times log2(e)
     float drop_c;         // keep scale 1/(1-p) rounded to float
     uint32_t drop_T;      // 16-bit drop threshold round(p * 65536)
@@ -50,6 +55,8 @@ hipError_t launch_bwd_dq16(Elem e, int d, bool causal, bool dropout, const BwdAr
                            hipStream_t stream);
 hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                              hipStream_t stream);
+// Combines the kv_splits partial results of a split forward into o and lse.
+hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream);
 hipError_t launch_dropout_mask(int64_t N, uint32_t T, uint32_t seed_lo, uint32_t seed_hi,
                                int64_t b, int64_t h, uint8_t *mask, hipStream_t stream);
 

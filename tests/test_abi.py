@@ -71,7 +71,7 @@ def test_invalid_params_rejected_before_launch(lib, kw, status):
     assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
 
 
-def test_bad_flags_and_reserved(lib):
+def test_bad_flags_and_key_length(lib):
     p = _p()
     p.causal = 2
     assert _fwd(lib, p) == fa.FA_EINVAL
@@ -79,8 +79,48 @@ def test_bad_flags_and_reserved(lib):
     p.out_f32 = 5
     assert _fwd(lib, p) == fa.FA_EINVAL
     p = _p()
-    p.reserved = 1
+    p.Nk = -1
     assert _fwd(lib, p) == fa.FA_EINVAL
+    # one head past 4 GiB (32-bit byte offsets)
+    p = _p(N=2**24, d=128)
+    assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
+    p = _p(N=16, d=128)
+    p.Nk = 2**24
+    assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
+
+
+def test_backward_needs_as_many_keys_as_queries(lib):
+    p = _p(N=16)
+    p.Nk = 17
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
+    assert lib.fa_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                      FAKE, 1 << 20, None) == fa.FA_EUNSUPPORTED
+    assert "keys" in lib.fa_last_error().decode()
+    p.Nk = 16   # Nk == N is the square case
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) > 0
+
+
+def test_split_forward_workspace_and_validation(lib):
+    B, H, N, d = 2, 3, 5, 64
+    p = _p(B=B, H=H, N=N, d=d)
+    p.Nk = 1000
+    sz = ctypes.c_size_t(-1).value
+    assert lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 0) == sz
+    assert lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 257) == sz
+    # one chunk (all 1000 keys fit 1024 = 16 * 64): plain forward, no workspace
+    assert lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 1) == 0
+    # 4 requested -> chunks of 256 keys, 4 used; O then LSE of every chunk
+    rows = B * H * N
+    o_bytes = (4 * rows * d * 4 + 255) // 256 * 256
+    lse_bytes = 4 * ((rows * 4 + 255) // 256 * 256)
+    assert lib.fa_fwd_splitkv_workspace_bytes(ctypes.byref(p), 4) == o_bytes + lse_bytes
+    for bad in (0, 257, -3):
+        assert lib.fa_fwd_splitkv(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, bad, FAKE,
+                                  1 << 30, None) == fa.FA_EINVAL
+    # workspace too small for the requested splits
+    assert lib.fa_fwd_splitkv(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+                              o_bytes, None) == fa.FA_EINVAL
+    assert "workspace" in lib.fa_last_error().decode()
 
 
 def test_null_and_misaligned_pointers(lib):

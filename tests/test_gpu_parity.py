@@ -149,6 +149,86 @@ def test_other_head_dims_fwd_bwd_full(gpu_lib, w):
         compare(name, got, exact, w.dtype)
 
 
+# ---------------------------- queries and keys of two lengths; split keys
+
+def compare_rows(name, got, exact, dtype):
+    """compare() over the rows that see at least one key; rows that see none
+    must be exactly O = 0 / LSE = -inf."""
+    e = np.asarray(exact)
+    g = got.detach().double().cpu().numpy()
+    lse_like = e.ndim == 3
+    dead = ~np.isfinite(e) if lse_like else np.zeros(e.shape, bool)
+    if lse_like:
+        assert np.all(g[dead] == -np.inf), "%s: rows with no visible key must be -inf" % name
+        compare(name, got.detach().cpu()[torch.from_numpy(~dead)], e[~dead], dtype)
+    else:
+        compare(name, got, e, dtype)
+
+
+CROSS = [
+    # dtype, d, N (queries), Nk (keys), causal, p
+    ("bf16", 128, 300, 1000, False, 0.0), ("bf16", 128, 300, 1000, True, 0.1),
+    ("bf16", 128, 1, 777, True, 0.0), ("bf16", 64, 1000, 300, True, 0.1),
+    ("bf16", 64, 77, 4096, False, 0.1), ("f16", 128, 130, 555, True, 0.0),
+    ("bf16", 96, 50, 333, True, 0.1), ("bf16", 256, 40, 300, True, 0.0),
+    ("f32", 64, 77, 200, True, 0.1), ("f32", 128, 33, 64, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CROSS, ids=["%s_d%d_%dx%d_c%d_p%g" % c for c in CROSS])
+def test_cross_lengths_fwd_full(gpu_lib, case):
+    """N != Nk (decoding, cross attention): every element of O and LSE,
+    causal aligned on the last key; queries that see no key give 0 / -inf."""
+    dt, d, N, Nk, causal, p = case
+    w = Workload("cross", 2, 2, N, d, dt, causal=causal, dropout_p=p, seed=17 + d + N,
+                 dropout_seed=0xFACE + Nk)
+    log("case %s Nk=%d" % (case, Nk))
+    q, k, v = workloads.draw_cross(w, Nk)
+    eo, el = oracle_fwd(w, q, k, v)
+    o, lse = run_fwd(gpu_lib, w, q, k, v)
+    compare_rows("O", o, eo, dt)
+    compare_rows("LSE", lse, el, dt)
+
+
+SPLITS = [
+    # dtype, d, N, Nk, causal, p, num_splits
+    ("bf16", 128, 1, 4096, True, 0.0, 8), ("bf16", 128, 16, 4096, True, 0.1, 64),
+    ("bf16", 128, 300, 1000, False, 0.1, 3), ("bf16", 64, 256, 2048, True, 0.0, 7),
+    ("bf16", 64, 1000, 300, True, 0.1, 2), ("f16", 128, 5, 3000, False, 0.0, 256),
+    ("bf16", 256, 17, 1500, True, 0.1, 5), ("f32", 64, 9, 1000, True, 0.1, 4),
+    ("bf16", 128, 1024, 1024, True, 0.1, 4),
+]
+
+
+@pytest.mark.parametrize("case", SPLITS, ids=["%s_d%d_%dx%d_c%d_p%g_s%d" % c for c in SPLITS])
+def test_split_keys_fwd_full(gpu_lib, case):
+    """fa_fwd_splitkv: key chunks on separate workgroups merged by their
+    log-sum-exp; every element of O and LSE against the oracle, and close to
+    the one-pass forward."""
+    dt, d, N, Nk, causal, p, splits = case
+    w = Workload("split", 2, 3, N, d, dt, causal=causal, dropout_p=p, seed=23 + d + N,
+                 dropout_seed=0xBEEF + Nk)
+    log("case %s" % (case,))
+    q, k, v = workloads.draw_cross(w, Nk)
+    eo, el = oracle_fwd(w, q, k, v)
+    dev = "cuda"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    for out_f32 in ((False, True) if dt != "f32" else (False,)):
+        o, lse = gpu_lib.fwd_splitkv(qd, kd, vd, splits, scale=w.softmax_scale, causal=causal,
+                                     dropout_p=p, seed=w.dropout_seed, out_f32=out_f32)
+        o1, lse1 = gpu_lib.fwd(qd, kd, vd, scale=w.softmax_scale, causal=causal, dropout_p=p,
+                               seed=w.dropout_seed, out_f32=out_f32)
+        torch.cuda.synchronize()
+        compare_rows("O", o, eo, dt)
+        compare_rows("LSE", lse, el, dt)
+        live = torch.isfinite(lse1)
+        assert torch.equal(torch.isfinite(lse), live)
+        # (16-bit paths sum the rounded probabilities, so the two summation
+        # orders differ at that rounding's level)
+        assert float((lse - lse1)[live].abs().max()) < (2e-3 if dt != "f32" else 1e-5)
+        assert float((o.float() - o1.float()).abs().max()) <= (2e-2 if dt != "f32" else 1e-5)
+
+
 def test_single_head_f32_fwd_bwd(gpu_lib):
     """B=1,H=1,N=128,d=64 fp32 non-causal forward and backward: max-abs 1e-5."""
     w = workloads.WORKLOADS["single_head_f32"]
