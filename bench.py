@@ -85,6 +85,35 @@ def time_steps(prob, steps, warmup, with_bwd=True):
     return wall, per
 
 
+def decode_line(fa, dev, B=1, H=32, N=16, Nk=65536, d=128, splits=16):
+    """Long-context decoding: N query rows over Nk keys per head, one pass
+    (B*H*ceil(N/256) workgroups) against the keys split into `splits`
+    chunks; HIP-event times and the K+V bytes read per second."""
+    w = workloads.Workload("decode", B, H, N, d, "bf16", causal=True, seed=6)
+    q, k, v = (t.to(dev) for t in workloads.draw_cross(w, Nk))
+    ws = torch.empty(max(fa.load().fa_fwd_splitkv_workspace_bytes(
+        __import__("ctypes").byref(fa.make_params(B, H, N, d, fa.BF16, causal=True, Nk=Nk)),
+        splits), 16), dtype=torch.uint8, device=dev)
+    runs = {"one_pass": lambda: fa.fwd(q, k, v, causal=True),
+            "split%d" % splits: lambda: fa.fwd_splitkv(q, k, v, splits, causal=True, workspace=ws)}
+    out = {"B": B, "H": H, "N": N, "Nk": Nk, "d": d}
+    kv_bytes = 2.0 * B * H * Nk * d * 2
+    for name, fn in runs.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        out[name + "_ms"] = round(ms, 4)
+        out[name + "_kv_GBs"] = round(kv_bytes / (ms * 1e-3) / 1e9, 1)
+    return out
+
+
 def traffic_for(kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -231,6 +260,7 @@ def main():
             del pd
             torch.cuda.empty_cache()
         extras["head_dims"] = hd
+        extras["decode"] = decode_line(fa, dev)
         log("extras %s" % extras)
 
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
