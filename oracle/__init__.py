@@ -69,6 +69,9 @@ def _bind(lib):
     lib.oracle_fwd_cross.argtypes = [i64, i64, i64, vp, vp, vp, dbl, i32, dbl, u64, i64, i64,
                                      vp, vp]
     lib.oracle_fwd_cross.restype = i32
+    lib.oracle_bwd_cross.argtypes = [i64, i64, i64, vp, vp, vp, vp, dbl, i32, dbl, u64, i64,
+                                     i64, vp, vp, vp, vp, vp]
+    lib.oracle_bwd_cross.restype = i32
     lib.oracle_probs.argtypes = [i64, i64, vp, vp, dbl, i32, dbl, u64, i64, i64, vp, vp]
     lib.oracle_probs.restype = i32
     lib.oracle_bwd_head.argtypes = [i64, i64, vp, vp, vp, vp, dbl, i32, dbl, u64, i64, i64,
@@ -216,6 +219,8 @@ def bwd(q, k, v, dout, scale: float, causal: bool = False, dropout_p: float = 0.
     lib = _load()
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, H, N, d = q.shape
+    if k.shape[2] != N:
+        return _bwd_cross(lib, q, k, v, dout, scale, causal, dropout_p, seed, heads)
     outs = [np.full((B, H, N, d), np.nan) for _ in range(4)]
     lse = np.full((B, H, N), np.nan)
     todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
@@ -231,3 +236,25 @@ def bwd(q, k, v, dout, scale: float, causal: bool = False, dropout_p: float = 0.
         lse[b, h] = lb
     dq, dk, dv, o = outs
     return dq, dk, dv, o, lse
+
+
+def _bwd_cross(lib, q, k, v, dout, scale, causal, dropout_p, seed, heads):
+    """bwd for Nq != Nk (k, v [B,H,Nk,d]): dq, o [B,H,Nq,d]; dk, dv [B,H,Nk,d]."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dq_all, o_all = np.full((B, H, Nq, d), np.nan), np.full((B, H, Nq, d), np.nan)
+    dk_all, dv_all = np.full((B, H, Nk, d), np.nan), np.full((B, H, Nk, d), np.nan)
+    lse = np.full((B, H, Nq), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        dq, o = np.zeros((Nq, d)), np.zeros((Nq, d))
+        dk, dv = np.zeros((Nk, d)), np.zeros((Nk, d))
+        lb = np.zeros(Nq)
+        qh, kh, vh, dh = (np.ascontiguousarray(x[b, h]) for x in (q, k, v, dout))
+        _check(lib.oracle_bwd_cross(Nq, Nk, d, _ptr(qh), _ptr(kh), _ptr(vh), _ptr(dh),
+                                    float(scale), int(bool(causal)), float(dropout_p),
+                                    seed & (2**64 - 1), b, h, _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(o), _ptr(lb)), "bwd_cross")
+        dq_all[b, h], dk_all[b, h], dv_all[b, h], o_all[b, h] = dq, dk, dv, o
+        lse[b, h] = lb
+    return dq_all, dk_all, dv_all, o_all, lse

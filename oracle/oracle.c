@@ -374,6 +374,86 @@ int oracle_bwd_head(int64_t N, int64_t d, const double *q, const double *k, cons
     return bad ? ORACLE_ENOMEM : ORACLE_OK;
 }
 
+/*
+ * Backward of one (b, h) head with Nq query rows and Nk keys (visibility and
+ * dropout counters as in oracle_fwd_cross).  Inputs q, dout: [Nq, d]; k, v:
+ * [Nk, d].  Outputs dq: [Nq, d]; dk, dv: [Nk, d]; o [Nq, d] and lse [Nq].
+ * The same calculus as oracle_bwd_head with P, Pd and dS materialised as
+ * Nq x Nk matrices.
+ */
+int oracle_bwd_cross(int64_t Nq, int64_t Nk, int64_t d, const double *q, const double *k,
+                     const double *v, const double *dout, double scale, int causal, double p,
+                     uint64_t seed, int64_t b, int64_t h, double *dq, double *dk, double *dv,
+                     double *o, double *lse)
+{
+    if (Nq < 0 || Nk < 0 || d <= 0 || !(p >= 0.0 && p < 1.0)) return ORACLE_EINVAL;
+    double c = p > 0.0 ? oracle_keep_scale(p) : 1.0;
+    uint32_t T = oracle_drop_threshold(p);
+    size_t nn = (size_t)(Nq > 0 ? Nq : 1) * (size_t)(Nk > 0 ? Nk : 1);
+    double *pd_all = (double *)malloc(sizeof(double) * nn);
+    double *ds_all = (double *)malloc(sizeof(double) * nn);
+    double *s = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+    double *prob = (double *)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+    if (!pd_all || !ds_all || !s || !prob) {
+        free(pd_all); free(ds_all); free(s); free(prob);
+        return ORACLE_ENOMEM;
+    }
+    /* Row pass (one query at a time): P, Pd, O_i, D_i, dS and dQ_i. */
+    for (int64_t i = 0; i < Nq; ++i) {
+        const double *qi = q + i * d, *doi = dout + i * d;
+        double *pd = pd_all + (size_t)i * (size_t)Nk, *ds = ds_all + (size_t)i * (size_t)Nk;
+        const int64_t last = causal ? i + (Nk - Nq) : Nk - 1;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < Nk; ++j) {
+            if (j > last) { s[j] = -INFINITY; continue; }
+            double acc = 0.0;
+            for (int64_t cc = 0; cc < d; ++cc) acc += qi[cc] * k[j * d + cc];
+            s[j] = acc * scale;
+            if (s[j] > m) m = s[j];
+        }
+        double li = -INFINITY;
+        if (m != -INFINITY) {
+            double l = 0.0;
+            for (int64_t j = 0; j < Nk; ++j)
+                if (s[j] != -INFINITY) l += exp(s[j] - m);
+            li = m + log(l);
+        }
+        lse[i] = li;
+        prob_row(Nk, s, li, p, seed, b, h, i, prob, pd);
+        double *oi = o + i * d;
+        for (int64_t cc = 0; cc < d; ++cc) oi[cc] = 0.0;
+        for (int64_t j = 0; j < Nk; ++j)
+            for (int64_t cc = 0; cc < d; ++cc) oi[cc] += pd[j] * v[j * d + cc];
+        double Di = 0.0;
+        for (int64_t cc = 0; cc < d; ++cc) Di += doi[cc] * oi[cc];
+        double *dqi = dq + i * d;
+        for (int64_t cc = 0; cc < d; ++cc) dqi[cc] = 0.0;
+        for (int64_t j = 0; j < Nk; ++j) {
+            if (prob[j] == 0.0) { ds[j] = 0.0; continue; }
+            double dpd = 0.0;
+            for (int64_t cc = 0; cc < d; ++cc) dpd += doi[cc] * v[j * d + cc];
+            double keep = p > 0.0 ? (double)keep_bit(seed, b, h, i, j, T) : 1.0;
+            ds[j] = prob[j] * (dpd * keep * c - Di);
+            for (int64_t cc = 0; cc < d; ++cc) dqi[cc] += scale * ds[j] * k[j * d + cc];
+        }
+    }
+    /* Column pass: dK_j and dV_j of each key. */
+    for (int64_t j = 0; j < Nk; ++j) {
+        double *dkj = dk + j * d, *dvj = dv + j * d;
+        for (int64_t cc = 0; cc < d; ++cc) { dkj[cc] = 0.0; dvj[cc] = 0.0; }
+        for (int64_t i = 0; i < Nq; ++i) {
+            double dsij = ds_all[(size_t)i * (size_t)Nk + (size_t)j];
+            double pdij = pd_all[(size_t)i * (size_t)Nk + (size_t)j];
+            for (int64_t cc = 0; cc < d; ++cc) {
+                dkj[cc] += scale * dsij * q[i * d + cc];
+                dvj[cc] += pdij * dout[i * d + cc];
+            }
+        }
+    }
+    free(pd_all); free(ds_all); free(s); free(prob);
+    return ORACLE_OK;
+}
+
 /* Number of threads OpenMP will use (for reporting). */
 int oracle_num_threads(void)
 {

@@ -50,6 +50,12 @@ MUTANTS = [
     ("cross_dropout_row_shifted", "prob_row(Nk, s, lse, p, seed, b, h, i, prob, pd);",
      "prob_row(Nk, s, lse, p, seed, b, h, i + (Nk - Nq), prob, pd);",
      [pins.test_cross_dropout_uses_the_square_counters]),
+    ("cross_bwd_dropout_scale_dropped", "ds[j] = prob[j] * (dpd * keep * c - Di);",
+     "ds[j] = prob[j] * (dpd * keep - Di);",
+     [lambda: pins.test_cross_gradients_match_finite_differences(3, 6, 2, True, 0.5)]),
+    ("cross_bwd_dk_row_index", "dkj[cc] += scale * dsij * q[i * d + cc];\n                dvj[cc] += pdij * dout[i * d + cc];\n            }\n        }\n    }\n    free(pd_all); free(ds_all); free(s); free(prob);",
+     "dkj[cc] += scale * dsij * q[(Nq - 1 - i) * d + cc];\n                dvj[cc] += pdij * dout[i * d + cc];\n            }\n        }\n    }\n    free(pd_all); free(ds_all); free(s); free(prob);",
+     [lambda: pins.test_cross_gradients_match_torch_fp64_autograd(5, 23, False)]),
 ]
 
 

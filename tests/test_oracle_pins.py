@@ -439,3 +439,53 @@ def test_cross_dropout_uses_the_square_counters():
     keep = oracle.dropout_mask(max(Nq, Nk), p, seed, 0, 0)[:Nq, :Nk]
     c = oracle.keep_scale(p)
     np.testing.assert_allclose(pd[0, 0, :, :Nk], prob[0, 0, :, :Nk] * keep * c, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.5])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk,d", [(1, 3, 2), (4, 2, 3), (3, 6, 2)])
+def test_cross_gradients_match_finite_differences(Nq, Nk, d, causal, p):
+    """Nq != Nk: analytic dQ, dK, dV agree with central differences of
+    L = sum(O * dO) (rows with no visible key contribute nothing)."""
+    seed, scale, eps = 77, 0.7, 1e-6
+    q, do = _rand((1, 1, Nq, d), 70), _rand((1, 1, Nq, d), 71)
+    k, v = _rand((1, 1, Nk, d), 72), _rand((1, 1, Nk, d), 73)
+    dq, dk, dv, o, lse = oracle.bwd(q, k, v, do, scale, causal, p, seed)
+    o_f, lse_f = oracle.fwd(q, k, v, scale, causal, p, seed)
+    np.testing.assert_array_equal(o, o_f)
+    np.testing.assert_array_equal(lse, lse_f)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args[name] = xp
+            lp = float(np.sum(oracle.fwd(args["q"], args["k"], args["v"], scale, causal, p, seed)[0] * do))
+            args[name] = xm
+            lm = float(np.sum(oracle.fwd(args["q"], args["k"], args["v"], scale, causal, p, seed)[0] * do))
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(5, 23), (23, 5)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_cross_gradients_match_torch_fp64_autograd(Nq, Nk, causal):
+    """Nq != Nk: torch's fp64 SDPA with the same visibility, differentiated by
+    autograd (rows with no visible key are left out of the loss)."""
+    d, scale = 6, 0.45
+    q, do = _rand((1, 2, Nq, d), 80), _rand((1, 2, Nq, d), 81)
+    k, v = _rand((1, 2, Nk, d), 82), _rand((1, 2, Nk, d), 83)
+    m = _cross_mask(Nq, Nk, causal)
+    live = m.any(axis=1)
+    do_live = do * live[None, None, :, None]
+    dq, dk, dv, _, _ = oracle.bwd(q, k, v, do_live, scale, causal)
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(m),
+                                                         scale=scale)
+    o = torch.where(torch.from_numpy(live)[None, None, :, None], o, torch.zeros_like(o))
+    (o * torch.from_numpy(do_live)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-12, atol=1e-13)
