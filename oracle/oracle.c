@@ -402,7 +402,7 @@ int oracle_bwd_cross(int64_t Nq, int64_t Nk, int64_t d, const double *q, const d
     for (int64_t i = 0; i < Nq; ++i) {
         const double *qi = q + i * d, *doi = dout + i * d;
         double *pd = pd_all + (size_t)i * (size_t)Nk, *ds = ds_all + (size_t)i * (size_t)Nk;
-        const int64_t last = causal ? i + (Nk - Nq) : Nk - 1;
+        const int64_t last = causal ? (Nk - Nq) + i : Nk - 1;   /* last visible key */
         double m = -INFINITY;
         for (int64_t j = 0; j < Nk; ++j) {
             if (j > last) { s[j] = -INFINITY; continue; }
@@ -434,7 +434,7 @@ int oracle_bwd_cross(int64_t Nq, int64_t Nk, int64_t d, const double *q, const d
             for (int64_t cc = 0; cc < d; ++cc) dpd += doi[cc] * v[j * d + cc];
             double keep = p > 0.0 ? (double)keep_bit(seed, b, h, i, j, T) : 1.0;
             ds[j] = prob[j] * (dpd * keep * c - Di);
-            for (int64_t cc = 0; cc < d; ++cc) dqi[cc] += scale * ds[j] * k[j * d + cc];
+            for (int64_t cc = 0; cc < d; ++cc) dqi[cc] += ds[j] * scale * k[j * d + cc];
         }
     }
     /* Column pass: dK_j and dV_j of each key. */
@@ -445,7 +445,7 @@ int oracle_bwd_cross(int64_t Nq, int64_t Nk, int64_t d, const double *q, const d
             double dsij = ds_all[(size_t)i * (size_t)Nk + (size_t)j];
             double pdij = pd_all[(size_t)i * (size_t)Nk + (size_t)j];
             for (int64_t cc = 0; cc < d; ++cc) {
-                dkj[cc] += scale * dsij * q[i * d + cc];
+                dkj[cc] += dsij * scale * q[i * d + cc];
                 dvj[cc] += pdij * dout[i * d + cc];
             }
         }

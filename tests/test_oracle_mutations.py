@@ -53,8 +53,8 @@ MUTANTS = [
     ("cross_bwd_dropout_scale_dropped", "ds[j] = prob[j] * (dpd * keep * c - Di);",
      "ds[j] = prob[j] * (dpd * keep - Di);",
      [lambda: pins.test_cross_gradients_match_finite_differences(3, 6, 2, True, 0.5)]),
-    ("cross_bwd_dk_row_index", "dkj[cc] += scale * dsij * q[i * d + cc];\n                dvj[cc] += pdij * dout[i * d + cc];\n            }\n        }\n    }\n    free(pd_all); free(ds_all); free(s); free(prob);",
-     "dkj[cc] += scale * dsij * q[(Nq - 1 - i) * d + cc];\n                dvj[cc] += pdij * dout[i * d + cc];\n            }\n        }\n    }\n    free(pd_all); free(ds_all); free(s); free(prob);",
+    ("cross_bwd_dk_row_index", "dkj[cc] += dsij * scale * q[i * d + cc];",
+     "dkj[cc] += dsij * scale * q[(Nq - 1 - i) * d + cc];",
      [lambda: pins.test_cross_gradients_match_torch_fp64_autograd(5, 23, False)]),
 ]
 
