@@ -89,9 +89,9 @@ typedef enum fa_dtype {
  *                visible to query i iff j <= i + (Nk - N), so the last query
  *                sees every key; a query with no visible key gets O = 0 and
  *                LSE = -inf.  Dropout counters use the query's own row i.
- *                The backward entry points need Nk == N (else
- *                FA_EUNSUPPORTED).  One head of q, k or v must stay below
- *                4 GiB (else FA_EUNSUPPORTED).
+ *                The backward takes the same Nk: dk, dv are [B,H,Nk,d].
+ *                One head of q, k or v must stay below 4 GiB (else
+ *                FA_EUNSUPPORTED).
  */
 typedef struct fa_params {
     int64_t B, H, N, d;
@@ -142,10 +142,10 @@ fa_status_t fa_fwd_splitkv(const fa_params_t *p, const void *q, const void *k, c
 size_t fa_bwd_workspace_bytes(const fa_params_t *p);
 
 /*
- * Backward.  Reads q, k, v and dout [B,H,N,d] in dtype, o (the forward's
- * output, in the forward's output type: dtype, or float32 when out_f32)
- * and lse (from fa_fwd); writes dq, dk, dv [B,H,N,d] (dtype, or float32
- * with out_f32).  `workspace` must hold at least
+ * Backward.  Reads q and dout [B,H,N,d], k and v [B,H,Nk,d] in dtype, o
+ * (the forward's output, in the forward's output type: dtype, or float32
+ * when out_f32) and lse (from fa_fwd); writes dq [B,H,N,d] and dk, dv
+ * [B,H,Nk,d] (dtype, or float32 with out_f32).  `workspace` must hold at least
  * fa_bwd_workspace_bytes(p) bytes; its contents on entry are ignored.  The
  * same p (scale, causal, dropout_p, seed) as the forward must be passed.
  */

@@ -177,15 +177,16 @@ def bwd_workspace_bytes(q, scale=None, causal=False, dropout_p=0.0, seed=0, out_
 
 def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dropout_p=0.0, seed=0,
         out_f32=False, workspace=None):
-    """Fused backward: returns (dq, dk, dv) with the forward's output type."""
+    """Fused backward: returns (dq, dk, dv) with the forward's output type
+    (k, v and so dk, dv may hold Nk != N keys)."""
     lib = load()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+    p = _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32)
+    for t, n in ((o, "o"), (dout, "dout")):
         _need(t, q, n)
-    p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
     out_dtype = torch.float32 if out_f32 else q.dtype
     dq = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    dk = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    dv = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    dk = torch.empty(k.shape, dtype=out_dtype, device=q.device)
+    dv = torch.empty(k.shape, dtype=out_dtype, device=q.device)
     need = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -205,7 +205,7 @@ fa_status_t fa_fwd_splitkv(const fa_params_t *p, const void *q, const void *k, c
 
 size_t fa_bwd_workspace_bytes(const fa_params_t *p) {
     bool empty = false;
-    if (check_params(p, &empty) != FA_OK || keys(p) != p->N) return (size_t)-1;
+    if (check_params(p, &empty) != FA_OK) return (size_t)-1;
     if (empty) return 0;
     return workspace_bytes(p);
 }
@@ -219,11 +219,7 @@ namespace {
 fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t workspace_size,
                       bool *empty, fa::BwdArgs *a) {
     fa_status_t s = check_params(p, empty);
-    if (s != FA_OK) return s;
-    if (keys(p) != p->N)
-        return fail(FA_EUNSUPPORTED, "the backward needs as many keys as queries (Nk=%d, N=%lld)",
-                    (int)p->Nk, (long long)p->N);
-    if (*empty) return s;
+    if (s != FA_OK || *empty) return s;
     if ((s = check_ptr(workspace, "workspace"))) return s;
     const size_t need = workspace_bytes(p);
     if (workspace_size < need)
@@ -234,6 +230,7 @@ fa_status_t bwd_setup(const fa_params_t *p, const void *workspace, size_t worksp
     a->nl2 = reinterpret_cast<float *>(reinterpret_cast<char *>(const_cast<void *>(workspace)) +
                                        row_array_bytes(p));
     a->B = p->B; a->H = p->H; a->N = p->N;
+    a->Nk = keys(p);
     a->scale = p->scale;
     a->scale_log2 = p->scale * 1.44269504088896340736f;
     const bool dropout = p->dropout_p > 0.f;

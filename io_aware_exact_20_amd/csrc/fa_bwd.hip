@@ -59,7 +59,9 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a, int64_t r
     for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
     if (row < rows && sub == 0) {
         a.dvec[row] = acc / a.drop_c;
-        a.nl2[row] = -a.lse[row] * kLog2e;
+        // A row that sees no key (LSE = -inf) gets -inf, so that its P is 0.
+        const float l = a.lse[row];
+        a.nl2[row] = l == -__builtin_huge_valf() ? l : -l * kLog2e;
     }
 }
 
@@ -95,11 +97,12 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
     const int64_t u = blockIdx.x;
     const int64_t bh = u % BH;
     const int64_t kblk = u / BH;                  // causal: low key blocks (most work) first
-    const int64_t N = a.N;
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const int64_t N = a.N, Nk = a.Nk;
+    const int64_t off = Nk - N;                   // causal: query i sees keys j <= i + off
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
     const T *__restrict__ Qg = reinterpret_cast<const T *>(a.q) + head;
-    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head;
-    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head_kv;
     const T *__restrict__ dOg = reinterpret_cast<const T *>(a.dout) + head;
     const float *__restrict__ lse_g = a.lse + (size_t)bh * (size_t)N;
     const float *__restrict__ dvec_g = a.dvec + (size_t)bh * (size_t)N;
@@ -113,7 +116,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
     frag_t<T> kf[NDC], vf[NDC];
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
-        if (key < N) {
+        if (key < Nk) {
             kf[c] = load_frag<T>(Kg + key * D + 16 * c + 8 * g);
             vf[c] = load_frag<T>(Vg + key * D + 16 * c + 8 * g);
         } else {
@@ -134,7 +137,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
         if (tid < BQ) {
             const int64_t q = q0 + tid;
             // Rows past N get P = exp2(-inf) = 0.
-            lse_r = q < N ? lse_g[q] * kLog2e : __builtin_huge_valf();
+            // (and rows that see no key, LSE = -inf)
+            lse_r = q < N && lse_g[q] != -__builtin_huge_valf() ? lse_g[q] * kLog2e
+                                                                : __builtin_huge_valf();
             dvec_r = q < N ? dvec_g[q] : 0.f;
         }
     };
@@ -144,8 +149,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
         if (tid < BQ) { lse2_s[buf][tid] = lse_r; dvec_s[buf][tid] = dvec_r; }
     };
 
-    const int64_t qstart = CAUSAL ? (k0 / BQ) * BQ : 0;
-    const int ntiles = (int)((N - qstart + BQ - 1) / BQ);
+    const int64_t qstart = CAUSAL ? (k0 - off > 0 ? (k0 - off) / BQ * BQ : 0) : 0;
+    const int ntiles = N > qstart ? (int)((N - qstart + BQ - 1) / BQ) : 0;
     load_rows(qstart);
     store_rows(0);
     __syncthreads();
@@ -157,7 +162,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
         const T *dos = dOs[buf];
         if (t + 1 < ntiles) load_rows(q0 + BQ);
 
-        const bool edge = (q0 + BQ > N) || (k0 + BK > N) || (CAUSAL && k0 + BK - 1 > q0);
+        const bool edge = (q0 + BQ > N) || (k0 + BK > Nk) || (CAUSAL && k0 + BK - 1 > q0 + off);
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             // ---- S = Q K^T and dP~ = dO V^T for this wavefront's 32 keys;
@@ -201,7 +206,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
                 float p = fast_exp2(fmaf(s[r], a.scale_log2, -lse2_s[buf][qi]));
                 if (edge) {
                     const int64_t q = q0 + qi;
-                    if (q >= N || key >= N || (CAUSAL && key > q)) p = 0.f;
+                    if (q >= N || key >= Nk || (CAUSAL && key > q + off)) p = 0.f;
                 }
                 float dpv = dp[r];
                 float pkv = p;
@@ -236,7 +241,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
     // column 32 db + 8(r/4) + 4g + r%4 of the lane's key row.
     const float vscale = DROPOUT ? a.drop_c : 1.f;
     const float kscale = DROPOUT ? a.scale * a.drop_c : a.scale;
-    if (key < N) {
+    if (key < Nk) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -247,11 +252,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
                 const float s0 = kscale * dk_acc[db][4 * rr], s1 = kscale * dk_acc[db][4 * rr + 1];
                 const float s2 = kscale * dk_acc[db][4 * rr + 2], s3 = kscale * dk_acc[db][4 * rr + 3];
                 if (a.out_f32) {
-                    store4<float>(reinterpret_cast<float *>(a.dv) + head + key * D + col, v0, v1, v2, v3);
-                    store4<float>(reinterpret_cast<float *>(a.dk) + head + key * D + col, s0, s1, s2, s3);
+                    store4<float>(reinterpret_cast<float *>(a.dv) + head_kv + key * D + col, v0, v1, v2, v3);
+                    store4<float>(reinterpret_cast<float *>(a.dk) + head_kv + key * D + col, s0, s1, s2, s3);
                 } else {
-                    store4<T>(reinterpret_cast<T *>(a.dv) + head + key * D + col, v0, v1, v2, v3);
-                    store4<T>(reinterpret_cast<T *>(a.dk) + head + key * D + col, s0, s1, s2, s3);
+                    store4<T>(reinterpret_cast<T *>(a.dv) + head_kv + key * D + col, v0, v1, v2, v3);
+                    store4<T>(reinterpret_cast<T *>(a.dk) + head_kv + key * D + col, s0, s1, s2, s3);
                 }
             }
     }
@@ -288,11 +293,12 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
     const int64_t u = blockIdx.x;
     const int64_t bh = u % BH;
     const int64_t qb = CAUSAL ? (nqb - 1 - u / BH) : (u / BH);
-    const int64_t N = a.N;
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const int64_t N = a.N, Nk = a.Nk;
+    const int64_t off = Nk - N;                   // causal: query i sees keys j <= i + off
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
     const T *__restrict__ Qg = reinterpret_cast<const T *>(a.q) + head;
-    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head;
-    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head_kv;
     const T *__restrict__ dOg = reinterpret_cast<const T *>(a.dout) + head;
     const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
 
@@ -311,20 +317,23 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
             df[c] = frag_t<T>{};
         }
     }
-    const float lse2 = qrow < N ? a.lse[(size_t)bh * (size_t)N + qrow] * kLog2e
+    const float lse_q = qrow < N ? a.lse[(size_t)bh * (size_t)N + qrow] : -__builtin_huge_valf();
+    // rows past N and rows that see no key (LSE = -inf): P = exp2(-inf) = 0
+    const float lse2 = lse_q != -__builtin_huge_valf() ? lse_q * kLog2e
                                 : __builtin_huge_valf();
     const float dvec = qrow < N ? a.dvec[(size_t)bh * (size_t)N + qrow] : 0.f;
 
-    const int64_t kend = CAUSAL ? (q0 + BQ < N ? q0 + BQ : N) : N;
-    const int ntiles = (int)((kend + BC - 1) / BC);
+    int64_t kend = CAUSAL ? q0 + BQ + off : Nk;
+    kend = kend < Nk ? kend : Nk;
+    const int ntiles = kend > 0 ? (int)((kend + BC - 1) / BC) : 0;
 
     TileCopy<T, BC, D, THREADS> kcopy, vcopy;
     f32x16 acc[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-    kcopy.load(Kg, 0, N, tid);
-    vcopy.load(Vg, 0, N, tid);
+    kcopy.load(Kg, 0, Nk, tid);
+    vcopy.load(Vg, 0, Nk, tid);
     kcopy.template store<LD>(Ks[0], tid);
     vcopy.template store<LD>(Vs[0], tid);
     __syncthreads();
@@ -334,11 +343,11 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
         const T *ks = Ks[buf];
         const T *vs = Vs[buf];
         if (t + 1 < ntiles) {
-            kcopy.load(Kg, (int64_t)(t + 1) * BC, N, tid);
-            vcopy.load(Vg, (int64_t)(t + 1) * BC, N, tid);
+            kcopy.load(Kg, (int64_t)(t + 1) * BC, Nk, tid);
+            vcopy.load(Vg, (int64_t)(t + 1) * BC, Nk, tid);
         }
         const int64_t k0 = (int64_t)t * BC;
-        const bool edge = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q0);
+        const bool edge = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0 + off);
 
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -358,7 +367,7 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
                 float p = fast_exp2(fmaf(s[r], a.scale_log2, -lse2));
                 if (edge) {
                     const int64_t kk = k0 + kb * 32 + 8 * (r / 4) + 4 * g + (r % 4);
-                    if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
+                    if (kk >= Nk || (CAUSAL && kk > qrow + off)) p = 0.f;
                 }
                 float dpv = dp[r];
                 if (DROPOUT) dpv = ((keep >> r) & 1u) ? dpv : 0.f;
@@ -410,7 +419,7 @@ static hipError_t launch_pre_t(const BwdArgs &a, hipStream_t stream) {
 template <typename T, int D>
 static hipError_t launch_dkdv_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
     using TL = DkdvTile<T, D>;
-    const int64_t units = a.B * a.H * ((a.N + TL::BK - 1) / TL::BK);
+    const int64_t units = a.B * a.H * ((a.Nk + TL::BK - 1) / TL::BK);
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
     if (causal) {

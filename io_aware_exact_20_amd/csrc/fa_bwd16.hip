@@ -70,11 +70,12 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
     const int64_t u = blockIdx.x;
     const int64_t bh = u % BH;
     const int64_t qb = CAUSAL ? (nqb - 1 - u / BH) : (u / BH);
-    const int N = (int)a.N;
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const int N = (int)a.N, Nk = (int)a.Nk;
+    const int64_t off = (int64_t)Nk - N;   // causal: row i sees keys j <= i + off
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
     const T *__restrict__ Qg = reinterpret_cast<const T *>(a.q) + head;
-    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head;
-    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head_kv;
     const T *__restrict__ dOg = reinterpret_cast<const T *>(a.dout) + head;
     const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
 
@@ -94,7 +95,9 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
             qf[nb][c] = load_frag<T>(Qg + (size_t)r * D + 16 * c + 8 * g);
             df[nb][c] = load_frag<T>(dOg + (size_t)r * D + 16 * c + 8 * g);
         }
-        lse2[nb] = row < N ? a.lse[(size_t)bh * (size_t)N + row] * kLog2eB : __builtin_huge_valf();
+        // rows past N and rows that see no key (LSE = -inf): P = exp2(-inf) = 0
+        const float l = row < N ? a.lse[(size_t)bh * (size_t)N + row] : -__builtin_huge_valf();
+        lse2[nb] = l != -__builtin_huge_valf() ? l * kLog2eB : __builtin_huge_valf();
         dvec[nb] = row < N ? a.dvec[(size_t)bh * (size_t)N + row] : 0.f;
     }
 
@@ -116,17 +119,19 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
     const int R0 = (wave * kWave + lane) / SW::CPR;
     const uint32_t gcol = (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0)) * 8);
     const uint32_t lane_boff = ((uint32_t)R0 * D + gcol) * 2;
-    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const uint32_t head_bytes = (uint32_t)Nk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, head_bytes), vrs = make_rsrc(Vg, head_bytes);
     auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
         buf2lds16(rs, lane_boff, (uint32_t)((t * BC + i * RSTEP) * D * 2),
                   buf + (wave + i * NW) * (kWave * 16));
     };
 
-    const int kend = CAUSAL ? (q0 + BQ < N ? q0 + BQ : N) : N;
-    const int NT = (kend + BC - 1) / BC;
-    const int wend = CAUSAL ? (q0w + RW < N ? q0w + RW : N) : N;
-    const int Tw = (wend + BC - 1) / BC;
+    auto tiles_to = [&](int64_t end) {
+        end = end < Nk ? end : Nk;
+        return end > 0 ? (int)((end + BC - 1) / BC) : 0;
+    };
+    const int NT = tiles_to(CAUSAL ? (int64_t)q0 + BQ + off : (int64_t)Nk);
+    const int Tw = tiles_to(CAUSAL ? (int64_t)q0w + RW + off : (int64_t)Nk);
 
     const float sl2 = a.scale_log2;
     f32x16 dq[NDB][2];
@@ -137,14 +142,14 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
 
     // Scores of block nb of tile t set to -inf where masked (edge tiles).
     auto is_edge = [&](int t, int nb) {
-        return (t * BC + BC > N) || (CAUSAL && t * BC + BC - 1 > q0w + 32 * nb);
+        return (t * BC + BC > Nk) || (CAUSAL && t * BC + BC - 1 > q0w + 32 * nb + off);
     };
     auto apply_mask = [&](f32x16 &s, int t, int nb) {
         const int k0 = t * BC;
-        int lim = N - 1 - (k0 + 4 * g);
+        int lim = Nk - 1 - (k0 + 4 * g);
         if (CAUSAL) {
-            const int c = q0w + 32 * nb + lq - (k0 + 4 * g);
-            lim = c < lim ? c : lim;
+            const int64_t c = (int64_t)q0w + 32 * nb + lq + off - (k0 + 4 * g);
+            lim = c < lim ? (int)(c > -64 ? c : -64) : lim;
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

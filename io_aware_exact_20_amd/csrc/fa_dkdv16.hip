@@ -101,17 +101,19 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     const int64_t u = blockIdx.x;
     const int64_t bh = u % BH;
     const int kblk = (int)(u / BH);                       // causal: low key blocks (most work) first
-    const int N = (int)a.N;
-    const size_t head = (size_t)bh * (size_t)N * D;
+    const int N = (int)a.N, Nk = (int)a.Nk;
+    const int off = Nk - N;                  // causal: query i sees keys j <= i + off
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
     const T *__restrict__ Qg = reinterpret_cast<const T *>(a.q) + head;
-    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head;
-    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head;
+    const T *__restrict__ Kg = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ Vg = reinterpret_cast<const T *>(a.v) + head_kv;
     const T *__restrict__ dOg = reinterpret_cast<const T *>(a.dout) + head;
     const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
 
     const int k0 = kblk * BK;                 // first key of the workgroup
     const int kp0 = k0 + pair * KP;           // first key of this pair
-    const int j0 = CAUSAL ? k0 / BQ : 0;      // first query tile
+    // first query tile (causal: the first row that sees key k0 is k0 - off)
+    const int j0 = CAUSAL ? (k0 - off > 0 ? (k0 - off) / BQ : 0) : 0;
     const int NTQ = (N + BQ - 1) / BQ - j0;   // query tiles streamed
 
     // ---- the pair's K (A) or V (B) rows: B operands, one key per lane, in AGPRs.
@@ -121,7 +123,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             int key = kp0 + 32 * kb + lq;
-            key = key < N ? key : N - 1;
+            key = key < Nk ? key : Nk - 1;
 #pragma unroll
             for (int c = 0; c < NDC; ++c) kv[kb][c] = load_frag<T>(src + (size_t)key * D + 16 * c + 8 * g);
         }
@@ -180,7 +182,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     // Masking of tile t for this pair: key > query (causal), key >= N, row >= N.
     auto is_edge = [&](int t) {
         const int qt0 = (j0 + t) * BQ;
-        return (qt0 + BQ > N) || (kp0 + KP > N) || (CAUSAL && kp0 + KP - 1 > qt0);
+        return (qt0 + BQ > N) || (kp0 + KP > Nk) || (CAUSAL && kp0 + KP - 1 > qt0 + off);
     };
     auto apply_mask = [&](f32x16 (&s)[2], int t) {
         const int qt0 = (j0 + t) * BQ;
@@ -190,7 +192,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int q = qt0 + 8 * (r / 4) + 4 * g + (r % 4);
-                if ((CAUSAL && key > q) || key >= N || q >= N) s[kb][r] = kNegInf;
+                if ((CAUSAL && key > q + off) || key >= Nk || q >= N) s[kb][r] = kNegInf;
             }
         }
     };
@@ -565,7 +567,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const int key = kp0 + 32 * kb + lq;
-        if (key < N) {
+        if (key < Nk) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -574,9 +576,9 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     const float x0 = osc * acc[db][kb][4 * rr + 0], x1 = osc * acc[db][kb][4 * rr + 1];
                     const float x2 = osc * acc[db][kb][4 * rr + 2], x3 = osc * acc[db][kb][4 * rr + 3];
                     if (a.out_f32)
-                        store4<float>(reinterpret_cast<float *>(dst) + head + (size_t)key * D + col, x0, x1, x2, x3);
+                        store4<float>(reinterpret_cast<float *>(dst) + head_kv + (size_t)key * D + col, x0, x1, x2, x3);
                     else
-                        store4<T>(reinterpret_cast<T *>(dst) + head + (size_t)key * D + col, x0, x1, x2, x3);
+                        store4<T>(reinterpret_cast<T *>(dst) + head_kv + (size_t)key * D + col, x0, x1, x2, x3);
                 }
         }
     }
@@ -585,7 +587,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 template <typename T, int D>
 static hipError_t launch_dkdv16_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
     using TL = Dkdv16Tile<T, D>;
-    const int64_t units = a.B * a.H * ((a.N + TL::BK - 1) / TL::BK);
+    const int64_t units = a.B * a.H * ((a.Nk + TL::BK - 1) / TL::BK);
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
     if (causal) {

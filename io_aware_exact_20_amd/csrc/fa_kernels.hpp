@@ -33,6 +33,7 @@ struct BwdArgs {
     float *dvec;          // workspace: D_i / c, D_i = dO_i . O_i, [B,H,N]
     float *nl2;           // workspace: -lse_i log2(e), [B,H,N]
     int64_t B, H, N;
+    int64_t Nk;           // keys per head (k, v, dk, dv are [B,H,Nk,d]); causal: key j <= i + Nk - N
     float scale;          // softmax scale
     float scale_log2;     // scale * log2(e)
     float drop_c;

@@ -89,15 +89,13 @@ def test_bad_flags_and_key_length(lib):
     assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
 
 
-def test_backward_needs_as_many_keys_as_queries(lib):
-    p = _p(N=16)
-    p.Nk = 17
-    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == ctypes.c_size_t(-1).value
-    assert lib.fa_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                      FAKE, 1 << 20, None) == fa.FA_EUNSUPPORTED
-    assert "keys" in lib.fa_last_error().decode()
-    p.Nk = 16   # Nk == N is the square case
-    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) > 0
+def test_backward_workspace_follows_the_query_rows(lib):
+    """The workspace holds per-query-row statistics: Nk does not change it."""
+    p = _p(B=2, H=3, N=100, d=64)
+    base = lib.fa_bwd_workspace_bytes(ctypes.byref(p))
+    for nk in (1, 17, 5000):
+        p.Nk = nk
+        assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == base
 
 
 def test_split_forward_workspace_and_validation(lib):

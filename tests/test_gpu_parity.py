@@ -190,6 +190,35 @@ def test_cross_lengths_fwd_full(gpu_lib, case):
     compare_rows("LSE", lse, el, dt)
 
 
+CROSS_BWD = [
+    # dtype, d, N (queries), Nk (keys), causal, p
+    ("bf16", 128, 300, 1000, True, 0.1), ("bf16", 128, 1000, 300, True, 0.0),
+    ("bf16", 64, 200, 777, False, 0.1), ("bf16", 64, 555, 130, True, 0.1),
+    ("f16", 128, 129, 64, True, 0.0), ("bf16", 96, 70, 250, True, 0.1),
+    ("bf16", 256, 40, 100, True, 0.0), ("f32", 64, 77, 200, True, 0.1),
+    ("f32", 128, 100, 33, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CROSS_BWD, ids=["%s_d%d_%dx%d_c%d_p%g" % c for c in CROSS_BWD])
+def test_cross_lengths_fwd_bwd_full(gpu_lib, case):
+    """N != Nk forward and backward (cross attention): every element of O,
+    LSE, dQ [N], dK and dV [Nk] against the oracle; queries that see no key
+    give O = 0, LSE = -inf and dQ = 0, and add nothing to dK, dV."""
+    dt, d, N, Nk, causal, p = case
+    w = Workload("crossb", 2, 2, N, d, dt, causal=causal, dropout_p=p, backward=True,
+                 seed=31 + d + N, dropout_seed=0xCAFE + Nk)
+    log("case %s" % (case,))
+    q, k, v, do = workloads.draw_cross(w, Nk, with_dout=True)
+    edq, edk, edv, eo, el = oracle_bwd(w, q, k, v, do)
+    o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
+    assert dk.shape == k.shape and dv.shape == v.shape and dq.shape == q.shape
+    compare_rows("O", o, eo, dt)
+    compare_rows("LSE", lse, el, dt)
+    for name, got, exact in (("dQ", dq, edq), ("dK", dk, edk), ("dV", dv, edv)):
+        compare(name, got, exact, dt)
+
+
 SPLITS = [
     # dtype, d, N, Nk, causal, p, num_splits
     ("bf16", 128, 1, 4096, True, 0.0, 8), ("bf16", 128, 16, 4096, True, 0.1, 64),

@@ -68,15 +68,20 @@ def draw(w: Workload, with_dout: bool | None = None, seed: int | None = None):
     return cast(q), cast(k), cast(v), cast(do)
 
 
-def draw_cross(w: Workload, Nk: int):
-    """q [B,H,N,d] and k, v [B,H,Nk,d] for attention over Nk keys: N(0,1)
-    draws in the order q, k, v from a CPU generator seeded with ``w.seed``,
-    cast to the workload's type with round-to-nearest-even."""
+def draw_cross(w: Workload, Nk: int, with_dout: bool = False):
+    """q [B,H,N,d] and k, v [B,H,Nk,d] (and dO [B,H,N,d]) for attention over
+    Nk keys: N(0,1) draws in the order q, k, v, dO from a CPU generator
+    seeded with ``w.seed``, cast to the workload's type with
+    round-to-nearest-even."""
     g = torch.Generator("cpu").manual_seed(w.seed)
     q = torch.randn((w.B, w.H, w.N, w.d), dtype=torch.float32, generator=g)
     k = torch.randn((w.B, w.H, Nk, w.d), dtype=torch.float32, generator=g)
     v = torch.randn((w.B, w.H, Nk, w.d), dtype=torch.float32, generator=g)
-    return q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype)
+    out = [q.to(w.torch_dtype), k.to(w.torch_dtype), v.to(w.torch_dtype)]
+    if with_dout:
+        out.append(torch.randn((w.B, w.H, w.N, w.d), dtype=torch.float32, generator=g)
+                   .to(w.torch_dtype))
+    return tuple(out)
 
 
 DROPOUT_SEED = 0x5EED000000000005
