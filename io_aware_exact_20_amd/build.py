@@ -32,7 +32,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 KERNEL_FLAGS = ["-fno-honor-nans"]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 PER_SOURCE = {"fa_fwd.hip": KERNEL_FLAGS + VGPR_FORM, "fa_bwd16.hip": KERNEL_FLAGS + VGPR_FORM,
-              "fa_dkdv16.hip": KERNEL_FLAGS}
+              "fa_dkdv16.hip": KERNEL_FLAGS + VGPR_FORM}
 
 
 def _compile(src: str) -> str:

@@ -10,11 +10,11 @@
 // this kernel produces dV = (keep c P)^T dO and dK = scale dS^T Q for one
 // block of keys per workgroup, streaming the query sequence.
 //
-// All matrix products of this file keep their accumulators in AGPRs (the
-// accumulation registers): the two 128 x 64 accumulators, the K or V
-// operands and the double-buffered scores of a wavefront fill the 256 AGPRs
-// at d = 128, and the ordinary VGPRs are left for the exponentials, the
-// rounded operands and LDS reads issued two groups ahead of their use.
+// Register files: the K or V operands of a wavefront are pinned to AGPRs
+// (the accumulation registers); this file is compiled with matrix-product
+// results in VGPRs, so the softmax and dS arithmetic reads the scores and dP
+// without v_accvgpr_read copies (the compiler places what does not fit, the
+// long-lived dV / dK accumulators first, in the remaining AGPRs).
 #include <type_traits>
 
 #include "fa_device.hpp"
