@@ -427,17 +427,43 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// acc += lo + hi of a packed pair of 16-bit values (exact products with 1).
+// acc + lo + hi of a packed pair of 16-bit values, in fp32 (the halves are
+// widened exactly).  Plain VALU adds: the dot-product instructions that
+// could do this in one step do not co-issue with the matrix products of the
+// same wavefront (measured: each costs about ten cycles of the product
+// pipeline), the widening and the adds do.
 template <typename T>
 __device__ __forceinline__ float sum2(uint32_t pair, float acc);
+// (The widened halves pass through an empty register constraint so that the
+// compiler does not fold the adds back into a dot-product instruction.)
 template <>
 __device__ __forceinline__ float sum2<bf16>(uint32_t pair, float acc) {
+    float lo = __builtin_bit_cast(float, pair << 16);
+    float hi = __builtin_bit_cast(float, pair & 0xFFFF0000u);
+    asm("" : "+v"(lo), "+v"(hi));
+    return (acc + lo) + hi;
+}
+template <>
+__device__ __forceinline__ float sum2<f16>(uint32_t pair, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_bit_cast(h2, pair);
+    float lo = (float)h[0], hi = (float)h[1];
+    asm("" : "+v"(lo), "+v"(hi));
+    return (acc + lo) + hi;
+}
+
+// The same sum as one dot-product instruction (v_dot2c_f32_bf16 / _f16):
+// no extra registers, but no co-issue with matrix products.
+template <typename T>
+__device__ __forceinline__ float sum2_dot(uint32_t pair, float acc);
+template <>
+__device__ __forceinline__ float sum2_dot<bf16>(uint32_t pair, float acc) {
     typedef __bf16 b2 __attribute__((ext_vector_type(2)));
     const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, pair), one, acc, false);
 }
 template <>
-__device__ __forceinline__ float sum2<f16>(uint32_t pair, float acc) {
+__device__ __forceinline__ float sum2_dot<f16>(uint32_t pair, float acc) {
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const h2 one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pair), one, acc, false);

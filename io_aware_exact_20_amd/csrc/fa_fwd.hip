@@ -257,8 +257,8 @@ fwd_kernel(const FwdArgs a) {
 // probability; otherwise the tile's probabilities are formed against the
 // stale reference, which is exact in real arithmetic and keeps every
 // probability below 256.  Row sums are taken on the rounded probabilities
-// that enter the product (v_dot2c_f32_bf16), so the output is a convex
-// combination of V rows with exactly the weights used.
+// that enter the product, so the output is a convex combination of V rows
+// with exactly the weights used.
 template <typename T, int D, int NW>
 struct Fwd16Tile {
     static constexpr int RW = 64;                 // query rows per wavefront
@@ -513,8 +513,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
             const float p1 = fast_exp2(fmaf(sc[nb][2 * i + 1], sl2, -mu[nb]));
             pp[nb][i] = pack2<T>(p0, p1);
             if (DROPOUT) {
-                // The row sums keep the dropped probabilities.
-                acc[nb][i & 1] = sum2<T>(pp[nb][i], acc[nb][i & 1]);
+                // The row sums keep the dropped probabilities.  (A single
+                // dot-product instruction: it costs product-pipeline cycles
+                // but, unlike the widening adds of sum2, no registers, which
+                // this variant has none to spare for.)
+                acc[nb][i & 1] = sum2_dot<T>(pp[nb][i], acc[nb][i & 1]);
                 const uint32_t m0 = ((keep_cur[nb] >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u;
                 const uint32_t m1 = ((keep_cur[nb] >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u;
                 pp[nb][i] &= (m0 | m1);
