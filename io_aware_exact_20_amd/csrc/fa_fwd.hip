@@ -422,12 +422,18 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     }
 
     // ---- building blocks.
-    // Keep bits of tile t: keep[nb] bit r <-> register r of score block nb.
+    // Keep decisions of tile t for score block nb, in the sign layout of
+    // keep_signs_from_blocks (pair i of the block in bits 15 - i, 31 - i).
+    const uint32_t kc2 = keep_cmp_const(a.drop_T);
     auto draw_keep = [&](uint32_t (&keep)[NB], int t) {
+        const uint32_t grp = (uint32_t)((klo + t * BC) >> 3) + 2 * (uint32_t)g;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            keep[nb] = keep_bits_row((uint32_t)(klo + t * BC), (uint32_t)(q0w + 32 * nb + lq), h_idx, b_idx,
-                                     a.seed_lo, a.seed_hi, a.drop_T);
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint32_t row = (uint32_t)(q0w + 32 * nb + lq);
+            const Philox4 b0 = philox4x32_10(grp, row, h_idx, b_idx, a.seed_lo, a.seed_hi);
+            const Philox4 b1 = philox4x32_10(grp + 1, row, h_idx, b_idx, a.seed_lo, a.seed_hi);
+            keep[nb] = keep_signs_from_blocks(b0, b1, kc2);
+        }
     };
     // Move the reference maxima when a tile exceeds them by the threshold.
     auto maybe_rescale = [&](const float (&mx)[NB]) {
@@ -518,9 +524,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
                 // but, unlike the widening adds of sum2, no registers, which
                 // this variant has none to spare for.)
                 acc[nb][i & 1] = sum2_dot<T>(pp[nb][i], acc[nb][i & 1]);
-                const uint32_t m0 = ((keep_cur[nb] >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u;
-                const uint32_t m1 = ((keep_cur[nb] >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u;
-                pp[nb][i] &= (m0 | m1);
+                // decisions of the pair in the sign bits of the two halves
+                const i16x2 sg = __builtin_bit_cast(i16x2, keep_cur[nb] << i);
+                pp[nb][i] &= __builtin_bit_cast(uint32_t, sg >> (i16x2){15, 15});
             }
             pin_vgpr(pp[nb][i]);   // keeps the work in its group (no sinking)
         };
