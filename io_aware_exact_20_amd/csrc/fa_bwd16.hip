@@ -166,8 +166,9 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
             const float p = fast_exp2(fmaf(s[r], sl2, -lse2[nb]));
             float dpv = dp[r];
             if (DROPOUT) {
-                // keep bit r sign-extended to a 32-bit mask: dP or +0.
-                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)keep, r, 1);
+                // keep decision of register r = 2i + e (bit 15 - i or 31 - i
+                // of the sign layout) sign-extended to a 32-bit mask: dP or +0.
+                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)keep, e ? 31 - i : 15 - i, 1);
                 dpv = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, dpv) & m);
             }
             ds[e] = p * (dpv - dvec[nb]);
@@ -176,7 +177,8 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         pin_vgpr(v);   // keeps the work in its group (no sinking)
         return v;
     };
-    // The keep bits of block nb of tile t (as keep_bits_row), drawn in stages:
+    // The keep decisions of block nb of tile t (those of keep_bits_row, in the
+    // sign layout of keep_signs_from_blocks), drawn in stages:
     // counters, then 20 block-rounds in order (unit u: round u/2 of block
     // u%2), then the bits, so that the rounds can sit between the dQ
     // products, which have no other VALU work.
@@ -201,7 +203,8 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
                 for (int q = 0; q < 4; ++q) pin_vgpr(k.c[h].x[q]);
         }
     };
-    auto keep_end = [&](KeepDraw &k) { return keep_bits_from_blocks(k.c[0], k.c[1], a.drop_T); };
+    const uint32_t kc2 = keep_cmp_const(a.drop_T);
+    auto keep_end = [&](KeepDraw &k) { return keep_signs_from_blocks(k.c[0], k.c[1], kc2); };
 
     // Scores of the lane's blocks: `cur` = the block being produced, `prv`
     // = the block whose dS is being formed.

@@ -156,31 +156,6 @@ __device__ __forceinline__ uint32_t keep_byte(uint32_t grp, uint32_t row, uint32
     return bits;
 }
 
-// Keep bits of the eight columns of a finished block (as keep_byte).
-__device__ __forceinline__ uint32_t keep_byte_of(const Philox4 &r, uint32_t threshold) {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        bits |= (uint32_t)((r.x[w] & 0xFFFFu) >= threshold) << (2 * w);
-        bits |= (uint32_t)((r.x[w] >> 16) >= threshold) << (2 * w + 1);
-    }
-    return bits;
-}
-
-// The sixteen bits of keep_bits_row from the lane's two finished blocks
-// (counters grp and grp + 1 of keep_bits_row), with the half-wavefront
-// exchange.
-__device__ __forceinline__ uint32_t keep_bits_from_blocks(const Philox4 &b0, const Philox4 &b1,
-                                                          uint32_t threshold) {
-    const uint32_t g = lane_in_wave() >> 5;
-    const uint32_t bits = keep_byte_of(b0, threshold) | (keep_byte_of(b1, threshold) << 8);
-    const uint32_t mine = g ? 4 : 0, theirs = g ? 0 : 4;
-    const uint32_t own = ((bits >> mine) & 0xFu) | (((bits >> (8 + mine)) & 0xFu) << 4);
-    const uint32_t send = ((bits >> theirs) & 0xFu) | (((bits >> (8 + theirs)) & 0xFu) << 4);
-    const uint32_t recv = other_half(send);
-    return g ? (recv | (own << 8)) : (own | (recv << 8));
-}
-
 // Keep masks of the two 16-bit lanes of a generator word: 0xFFFF in each half
 // whose lane value is at least the threshold T, 0 elsewhere, for both halves
 // at once.  Flipping the top bits maps the unsigned order of the lanes onto
