@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, causal, d=128) + % of MFMA peak"
 # Sources of the 16-bit kernels each stage runs (the counters in
 # profiles/traffic.json are only used while these are unchanged).
-KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "bwd_dkdv": "fa_dkdv16.hip", "bwd_dq": "fa_bwd16.hip"}
+KERNEL_SOURCES = {"fwd": "fa_fwd_pp.hip", "bwd_dkdv": "fa_dkdv16.hip", "bwd_dq": "fa_bwd16.hip"}
 COPY_BYTES = 1 << 30             # the plain copy used to calibrate the HBM byte counters
 
 
@@ -236,12 +236,43 @@ def main():
                                                     + per0["bwd_dq"]) * 1e-3) / 1e12, 2)
         extras["p0_fwdbwd_tflops"] = round(3.5 * F / (wall0 * 1e-3) / 1e12, 2)
         del p0
-        w4 = workloads.WORKLOADS["long_causal_4k"]
-        p4 = make_problem(fa, w4, dev, with_bwd=False)
-        _, per4 = time_steps(p4, max(10, args.steps), 3, with_bwd=False)
-        extras["long4k_fwd_tflops"] = round(w4.flops_fwd() / (per4["fwd"] * 1e-3) / 1e12, 2)
+        # Long-context causal forward, N swept over 4096, 16384, 65536: per-N
+        # throughput and the HBM the call adds (only O and LSE; the library
+        # allocates nothing, so the allocator's peak does not move during it).
+        longs = {}
+        for name in ("long_causal_4k", "long_causal_16k", "long_causal_64k"):
+            wl = workloads.WORKLOADS[name]
+            before = torch.cuda.memory_allocated()
+            pl = make_problem(fa, wl, dev, with_bwd=False)
+            out_bytes = pl.o.numel() * pl.o.element_size() + pl.lse.numel() * 4
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats()
+            peak0 = torch.cuda.max_memory_allocated()
+            reps = 10 if wl.N <= 16384 else 3
+            _, perl = time_steps(pl, reps, 2, with_bwd=False)
+            longs[str(wl.N)] = {
+                "fwd_tflops": round(wl.flops_fwd() / (perl["fwd"] * 1e-3) / 1e12, 2),
+                "fwd_ms": round(perl["fwd"], 4),
+                "out_bytes": out_bytes,
+                "allocated_during_call": torch.cuda.max_memory_allocated() - peak0,
+                "score_matrix_bytes": workloads.score_matrix_bytes(wl.N, wl.B * wl.H),
+                "inputs_bytes": torch.cuda.memory_allocated() - before - out_bytes,
+            }
+            del pl
+            torch.cuda.empty_cache()
+        extras["long_causal"] = longs
+        extras["long4k_fwd_tflops"] = longs["4096"]["fwd_tflops"]
         extras["long4k_fwd_pct_peak"] = round(100 * extras["long4k_fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
-        del p4
+        # Small forward (2 x 8 x 1024 x 64), non-causal and causal.
+        small = {}
+        for name in ("small_fwd_bf16", "small_fwd_bf16_causal"):
+            ws_ = workloads.WORKLOADS[name]
+            ps = make_problem(fa, ws_, dev, with_bwd=False)
+            _, pers = time_steps(ps, 20, 3, with_bwd=False)
+            small[name] = {"fwd_tflops": round(ws_.flops_fwd() / (pers["fwd"] * 1e-3) / 1e12, 2),
+                           "fwd_ms": round(pers["fwd"], 4)}
+            del ps
+        extras["small_fwd"] = small
         w3 = workloads.WORKLOADS["mid_fwdbwd_causal"]
         p3 = make_problem(fa, w3, dev)
         wall3, _ = time_steps(p3, max(5, args.steps // 2), 2)

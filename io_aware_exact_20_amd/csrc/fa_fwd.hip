@@ -28,6 +28,14 @@
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
+#ifndef FA_FWD_KH0
+#define FA_FWD_KH0 (2 * SB)
+#endif
+
+#ifndef FA_FWD_PP
+#define FA_FWD_PP 1   // d = 128, 16-bit: two wavefronts per SIMD in opposite phases
+#endif
+
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 4   // wavefronts per workgroup of the 16-bit forward
 #endif
@@ -435,6 +443,29 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
             keep[nb] = keep_signs_from_blocks(b0, b1, kc2);
         }
     };
+    // The same draw split into its 40 generator rounds (four blocks of ten),
+    // so that the rounds of tile t+1 can ride between the products of step t.
+    struct KeepDraw { Philox4 c[2 * NB]; };
+    auto keep_begin = [&](KeepDraw &k, int t) {
+        const uint32_t grp = (uint32_t)((klo + t * BC) >> 3) + 2 * (uint32_t)g;
+#pragma unroll
+        for (int s = 0; s < 2 * NB; ++s) {
+            k.c[s].x[0] = grp + (s & 1);
+            k.c[s].x[1] = (uint32_t)(q0w + 32 * (s >> 1) + lq);
+            k.c[s].x[2] = h_idx;
+            k.c[s].x[3] = b_idx;
+        }
+    };
+    auto keep_rounds = [&](KeepDraw &k, int u0, int u1) {
+#pragma unroll
+        for (int u = u0; u < u1; ++u) philox_round(k.c[u % (2 * NB)], u / (2 * NB), a.seed_lo, a.seed_hi);
+        if (u1 > u0) {
+#pragma unroll
+            for (int s = 0; s < 2 * NB; ++s)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pin_vgpr(k.c[s].x[q]);
+        }
+    };
     // Move the reference maxima when a tile exceeds them by the threshold.
     auto maybe_rescale = [&](const float (&mx)[NB]) {
         bool need = false;
@@ -468,7 +499,13 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
     constexpr int SB = NDC;                  // K fragment groups (2 products each)
     constexpr int SC = 2 * NDB;              // V fragment groups (2 products each)
     static_assert(SB == 8 || SB == 4, "group plan for d = 128 or 64");
-    constexpr int PB = 12;                   // pairs computed in B
+    constexpr int PB = 10;                   // pairs computed in B
+    constexpr int PC = 16 - PB;              // pairs computed in C
+    static_assert(PB >= 8, "chunk 0's pairs must be complete before C's first product");
+    // Half-groups that carry the generator rounds of the next tile's keep
+    // decisions (NKR rounds in all).
+    constexpr int NKR = 10 * 2 * NB;
+    constexpr int KH0 = FA_FWD_KH0, KH1 = 2 * SB + 2 * SC;
     uint32_t keep_cur[NB];
     // kp: the first two K fragments of tile t+1, read during the previous
     // step (K tiles are loaded three steps ahead, so tile t+1 is complete
@@ -512,29 +549,31 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
         float acc[NB][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) { acc[nb][0] = 0.f; acc[nb][1] = 0.f; }
+        // Keep decisions of tile t+1: the 40 generator rounds are spread over
+        // the half-groups [KH0, KH1) of this step (B: 0 .. 2 SB - 1, C: 2 SB
+        // .. 2 SB + 2 SC - 1).
+        KeepDraw kd;
+        if (DROPOUT) keep_begin(kd, t + 1);
+        auto spread = [&](int hg) {
+            if (DROPOUT && hg >= KH0 && hg < KH1)
+                keep_rounds(kd, (NKR * (hg - KH0)) / (KH1 - KH0), (NKR * (hg - KH0 + 1)) / (KH1 - KH0));
+        };
         // Pair p = (row block p & 1, registers 2i, 2i+1 with i = p >> 1).
         auto pair = [&](int p) {
             const int nb = p & 1, i = p >> 1;
             const float p0 = fast_exp2(fmaf(sc[nb][2 * i], sl2, -mu[nb]));
             const float p1 = fast_exp2(fmaf(sc[nb][2 * i + 1], sl2, -mu[nb]));
             pp[nb][i] = pack2<T>(p0, p1);
+            // Row sums of the fp32 probabilities (dropped ones included):
+            // two adds that co-issue with the products and need no
+            // registers beyond p0, p1.
+            acc[nb][i & 1] = (acc[nb][i & 1] + p0) + p1;
             if (DROPOUT) {
-                // The row sums keep the dropped probabilities.  (A single
-                // dot-product instruction: it costs product-pipeline cycles
-                // but, unlike the widening adds of sum2, no registers, which
-                // this variant has none to spare for.)
-                acc[nb][i & 1] = sum2_dot<T>(pp[nb][i], acc[nb][i & 1]);
                 // decisions of the pair in the sign bits of the two halves
                 const i16x2 sg = __builtin_bit_cast(i16x2, keep_cur[nb] << i);
                 pp[nb][i] &= __builtin_bit_cast(uint32_t, sg >> (i16x2){15, 15});
             }
             pin_vgpr(pp[nb][i]);   // keeps the work in its group (no sinking)
-        };
-        auto rowsum = [&](int w) {   // w = pair index
-            if (!DROPOUT) {
-                const int nb = w & 1, i = w >> 1;
-                acc[nb][i & 1] = sum2<T>(pp[nb][i], acc[nb][i & 1]);
-            }
         };
         float mxp[NB];
 #pragma unroll
@@ -545,7 +584,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
                 mxp[nb] = fmaxf(mxp[nb], fmaxf(sn[nb][2 * w], sn[nb][2 * w + 1]));
         };
 
-        // ---- B: S of tile t+1 | pairs 0..11 | K loads of tile t+3.
+        // ---- B: S of tile t+1 | pairs 0..11 | K loads of tile t+3, V loads of t+1.
         frag_t<T> kf[3], vf[3];
         kf[0] = kp[0];
         kf[1] = kp[1];
@@ -559,29 +598,30 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
             }
 #pragma unroll
             for (int p = (2 * j * PB) / (2 * SB); p < ((2 * j + 1) * PB) / (2 * SB); ++p) pair(p);
+            spread(2 * j);
             __builtin_amdgcn_sched_barrier(0);
             // Half-group 2j+1: row block 1.
             if (HN) mma(sn[1], kf[j % 3], qf[1][j]);
 #pragma unroll
             for (int p = ((2 * j + 1) * PB) / (2 * SB); p < ((2 * j + 2) * PB) / (2 * SB); ++p) pair(p);
+            spread(2 * j + 1);
             if (j < LOADS) load_part(krs, t + 3, kbuf(KL), j);
+            if (j >= LOADS && j < 2 * LOADS) load_part(vrs, t + 1, vbuf(VB ^ 1), j - LOADS);
             if (j == SB - 2) vf[0] = vfrag(0);
             if (j == SB - 1) vf[1] = vfrag(1);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (HN && is_edge(t + 1)) apply_mask(sn, t + 1);
 
-        // ---- C: PV of tile t | pairs 12..15, row sums, maxima of t+1 | V loads of t+1.
+        // ---- C: PV of tile t | pairs 12..15, row sums, maxima of t+1.
         // Work of half-group k (one product each, k = 0 .. 2 SC - 1): pairs
         // 12..15 over the first SC halves (before chunk 1's products), the
         // 16 row sums and the 8 maxima spread over all of them.
         auto cwork = [&](int k) {
             if (k < SC) {
 #pragma unroll
-                for (int p = PB + (k * 4) / SC; p < PB + ((k + 1) * 4) / SC; ++p) pair(p);
+                for (int p = PB + (k * PC) / SC; p < PB + ((k + 1) * PC) / SC; ++p) pair(p);
             }
-#pragma unroll
-            for (int w = (k * 16) / (2 * SC); w < ((k + 1) * 16) / (2 * SC); ++w) rowsum(w);
             if (HN) {
 #pragma unroll
                 for (int w = (k * 8) / (2 * SC); w < ((k + 1) * 8) / (2 * SC); ++w) maxpair(w);
@@ -593,10 +633,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
             const int cc = j / NDB, db = j % NDB;
             mma(o[db][0], vf[j % 3], pfrag(0, cc));
             cwork(2 * j);
+            spread(2 * SB + 2 * j);
             __builtin_amdgcn_sched_barrier(0);
             mma(o[db][1], vf[j % 3], pfrag(1, cc));
             cwork(2 * j + 1);
-            if (j < LOADS) load_part(vrs, t + 1, vbuf(VB ^ 1), j);
+            spread(2 * SB + 2 * j + 1);
             if (j == SC - 2) kp[0] = lds_frag<T>(kql + koff[0]);
             if (j == SC - 1) kp[1] = lds_frag<T>(kql + koff[1]);
             if (j == SC - 1) {
@@ -615,7 +656,11 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd16_kernel(const FwdArgs a) {
         if (HN) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) mx[nb] = mxp[nb];
-            if (DROPOUT) draw_keep(keep_cur, t + 1);
+            if (DROPOUT) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    keep_cur[nb] = keep_signs_from_blocks(kd.c[2 * nb], kd.c[2 * nb + 1], kc2);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of K_{t+3}, V_{t+1} landed
         __syncthreads();                 // ... everyone's; buffers of K_{t+1}, V_t free
@@ -827,15 +872,18 @@ hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream)
 
 hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                       hipStream_t stream) {
-    // d = 64 and 128 with 16-bit inputs take the 64-rows-per-wavefront
-    // kernel; every other case the generic one (32 rows per wavefront).
+    // 16-bit inputs: d = 128 takes the two-wavefronts-per-SIMD kernel
+    // (fa_fwd_pp.hip), d = 64 the 64-rows-per-wavefront kernel; every other
+    // case the generic one (32 rows per wavefront).
     switch (e) {
     case Elem::BF16:
         switch (d) {
         case 32: return launch_fwd_t<bf16, 32>(causal, dropout, a, stream);
         case 64: return launch_fwd16_t<bf16, 64, FA_FWD_NW>(causal, dropout, a, stream);
         case 96: return launch_fwd_t<bf16, 96>(causal, dropout, a, stream);
-        case 128: return launch_fwd16_t<bf16, 128, FA_FWD_NW>(causal, dropout, a, stream);
+        case 128:
+            if (FA_FWD_PP) return launch_fwd_pp(e, d, causal, dropout, a, stream);
+            return launch_fwd16_t<bf16, 128, FA_FWD_NW>(causal, dropout, a, stream);
         case 256: return launch_fwd_t<bf16, 256>(causal, dropout, a, stream);
         }
         break;
@@ -844,7 +892,9 @@ hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a
         case 32: return launch_fwd_t<f16, 32>(causal, dropout, a, stream);
         case 64: return launch_fwd16_t<f16, 64, FA_FWD_NW>(causal, dropout, a, stream);
         case 96: return launch_fwd_t<f16, 96>(causal, dropout, a, stream);
-        case 128: return launch_fwd16_t<f16, 128, FA_FWD_NW>(causal, dropout, a, stream);
+        case 128:
+            if (FA_FWD_PP) return launch_fwd_pp(e, d, causal, dropout, a, stream);
+            return launch_fwd16_t<f16, 128, FA_FWD_NW>(causal, dropout, a, stream);
         case 256: return launch_fwd_t<f16, 256>(causal, dropout, a, stream);
         }
         break;

@@ -1,0 +1,389 @@
+// Forward of fused exact attention for 16-bit inputs at d = 128 on gfx950,
+// with two wavefronts per SIMD working in opposite phases.
+//
+// The method is the one of the other forward kernels: Q, K, V tiled into
+// on-chip blocks, the online-softmax recurrence (running row maximum,
+// normaliser, rescaled output accumulator) over key tiles, and only O and
+// the per-row log-sum-exp written back ("Tiling" and "Recomputation",
+// mrodiduger.github.io page; steps 1-4 of "Architecture, step by step",
+// interviewsvector.com page).
+//
+// Schedule.  A workgroup of eight wavefronts owns 256 query rows, 32 per
+// wavefront; K and V tiles of 32 keys are shared through LDS.  A step
+// (one tile) of a wavefront has a matrix phase -- S of the next tile
+// (S^T = K Q^T, eight 32x32x16 products) and O^T += V^T P^T of the current
+// one (eight products) -- and a vector phase -- masking, row maxima, the
+// lazy rescale, exponentials, row sums, rounding and dropout of the next
+// tile's scores.  Wavefronts 0-3 run matrix then vector phase, wavefronts
+// 4-7 vector then matrix phase, and the two wavefronts on one SIMD (w and
+// w + 4) belong to different halves, so while one of them keeps the matrix
+// core busy the other one does its softmax arithmetic on the vector ALU
+// (the ping-pong arrangement the flash-attention-4 page describes for
+// overlapping softmax with the matrix products, applied to wavefronts
+// sharing a SIMD).  One barrier per step keeps the halves aligned.
+//
+// Layout of the products, as in the other 16-bit forward: scores are
+// formed transposed, S^T = K Q^T, so a lane owns one query row and sixteen
+// keys of a tile; the rounded scores are directly the B operand of
+// O^T += V^T P^T; V^T comes from the row-major LDS tile through
+// ds_read_b64_tr_b16.  Tiles reach LDS by direct buffer loads (XOR-swizzled
+// 16-byte chunks, zeros past the last key).
+#include <type_traits>
+
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+template <typename T, int D>
+struct FwdPPTile {
+    static constexpr int NW = 8;                          // wavefronts, two per SIMD
+    static constexpr int BQ = 32 * NW;                    // query rows per workgroup
+    static constexpr int BC = 32;                         // keys per tile
+    static constexpr int THREADS = NW * kWave;
+    static constexpr int TILE_BYTES = BC * D * 2;         // one K or V tile
+    static constexpr int CHUNK_BYTES = kWave * 16;        // one wavefront load instruction
+    static constexpr int CHUNKS = TILE_BYTES / CHUNK_BYTES;   // per tile
+    static constexpr int LOADS = 2 * CHUNKS / NW;         // per wavefront per step (K and V)
+};
+
+// Lazy-rescale threshold (log2 units), as in the other forward kernels.
+constexpr float kPPRescaleLog2 = 8.0f;
+
+template <typename T, int D, bool CAUSAL, bool DROPOUT>
+__global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
+    using TL = FwdPPTile<T, D>;
+    using SW = Swz<D>;
+    constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW;
+    constexpr int TB = TL::TILE_BYTES, CB = TL::CHUNK_BYTES, CHUNKS = TL::CHUNKS, LOADS = TL::LOADS;
+    constexpr int RB = SW::ROW_BYTES;
+    constexpr int RPC = CB / RB;      // tile rows per load instruction
+    constexpr int NDC = D / 16;       // contraction chunks of S
+    constexpr int NDB = D / 32;       // 32-column blocks of O
+    constexpr float kNegInf = -__builtin_huge_valf();
+    static_assert(D == 128, "tile plan for d = 128");
+    static_assert(2 * CHUNKS == LOADS * NW && LOADS >= 1, "load split");
+    static_assert(2 * NDB == NDC, "one V^T product per K product");
+
+    // LDS: K tile t in buffer t & 1, V tile t in buffer t & 1.
+    __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], vs0[TB], vs1[TB];
+
+    const int lane = (int)lane_in_wave();
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lq = lane & 31, g = lane >> 5;
+    // Wavefronts w and w + 4 share a SIMD and own adjacent 32-row blocks.
+    const int order = wave >> 2;                      // 0: matrix phase first
+    const int rblk = 2 * (wave & 3) + order;
+
+    const int64_t BH = a.B * a.H;
+    const int64_t nqb = (a.N + BQ - 1) / BQ;
+    const int64_t u = blockIdx.x;
+    const int64_t bh = u % BH;
+    const int64_t qi = (u / BH) / a.kv_splits;
+    const int split = (int)((u / BH) % a.kv_splits);
+    const int64_t qb = CAUSAL ? (nqb - 1 - qi) : qi;
+    const int N = (int)a.N, Nk = (int)a.Nk;
+    const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
+    const T *__restrict__ Q = reinterpret_cast<const T *>(a.q) + head;
+    const T *__restrict__ K = reinterpret_cast<const T *>(a.k) + head_kv;
+    const T *__restrict__ V = reinterpret_cast<const T *>(a.v) + head_kv;
+    const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
+
+    const int q0 = (int)qb * BQ;
+    const int q0w = q0 + 32 * rblk;                    // first query row of this wavefront
+    const int qrow = q0w + lq;                         // this lane's query row
+    const int klo = split * a.kv_chunk;
+    const int khi = (int)((int64_t)klo + a.kv_chunk < (int64_t)Nk ? klo + a.kv_chunk : Nk);
+    const int64_t off = (int64_t)Nk - N;
+
+    // Q fragments (B operand of S^T = K Q^T), rows clamped into range.
+    frag_t<T> qf[NDC];
+    {
+        const int r = qrow < N ? qrow : N - 1;
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) qf[c] = load_frag<T>(Q + (size_t)r * D + 16 * c + 8 * g);
+    }
+
+    // LDS read offsets: K fragments along a key row; V^T by transposed reads.
+    uint32_t koff[NDC];
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) koff[c] = SW::off(lq, 16 * c + 8 * g);
+    uint32_t voff[2][NDB];
+    {
+        const int G = lane >> 4, k = (lane >> 2) & 3, j = lane & 3;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                voff[hf][db] = SW::off(8 * hf + 4 * (G >> 1) + k, 32 * db + 16 * (G & 1) + 4 * j);
+    }
+
+    // Tile loads.  Load instruction L (0 .. 2 CHUNKS - 1) of a step fills
+    // rows RPC (L % CHUNKS) .. of the K (L < CHUNKS) or V tile; this
+    // wavefront issues L = wave + i NW.  Lane l loads the logical 16-byte
+    // chunk that the swizzle places at position l % CPR of its row.
+    uint32_t lboff[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int L = wave + i * NW;
+        const int r = RPC * (L % CHUNKS) + lane / SW::CPR;
+        lboff[i] = ((uint32_t)r * D + (uint32_t)(((lane % SW::CPR) ^ (int)SW::f((uint32_t)r)) * 8)) * 2;
+    }
+    const uint32_t head_bytes = (uint32_t)Nk * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
+    // Buffers by parity (compile-time wherever tiles are read, so that the
+    // compiler can tell the loads into one buffer from reads of the other).
+    auto kbuf = [&](int par) { return par ? (lds_char *)ks1 : (lds_char *)ks0; };
+    auto vbuf = [&](int par) { return par ? (lds_char *)vs1 : (lds_char *)vs0; };
+    // This wavefront's share of the loads of K tile tk and V tile tv (into
+    // the buffers of their parities).
+    auto load_step = [&](int tk, int tv) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int L = wave + i * NW;
+            const int c = L % CHUNKS;
+            if (L < CHUNKS)
+                buf2lds16(krs, lboff[i], (uint32_t)((klo + tk * BC) * D * 2), kbuf(tk & 1) + c * CB);
+            else
+                buf2lds16(vrs, lboff[i], (uint32_t)((klo + tv * BC) * D * 2), vbuf(tv & 1) + c * CB);
+        }
+    };
+
+    auto tiles_to = [&](int64_t end) {
+        end = end < khi ? end : khi;
+        return end > klo ? (int)((end - klo + BC - 1) / BC) : 0;
+    };
+    const int NT = tiles_to(CAUSAL ? (int64_t)q0 + BQ + off : (int64_t)Nk);   // workgroup
+    const int Tw = tiles_to(CAUSAL ? (int64_t)q0w + 32 + off : (int64_t)Nk);  // this wavefront
+
+    // Tile t needs masking if it reaches past the last key or, causal, past
+    // what the wavefront's first row sees.
+    auto is_edge = [&](int t) {
+        const int64_t k0 = (int64_t)klo + t * BC;
+        return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + off);
+    };
+    // Register r holds key k0 + 4g + kk(r), kk(r) = 8(r/4) + r%4, for query
+    // row qrow; masked: key >= Nk, or (causal) key > qrow + off.
+    auto apply_mask = [&](f32x16 &s, int t) {
+        const int k0 = klo + t * BC;
+        int lim = Nk - 1 - (k0 + 4 * g);
+        if (CAUSAL) {
+            const int64_t c = (int64_t)qrow + off - (k0 + 4 * g);
+            lim = c < lim ? (int)(c > -64 ? c : -64) : lim;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r / 4) + (r % 4);
+            if (kk > lim) s[r] = kNegInf;
+        }
+    };
+
+    const float sl2 = a.scale_log2;
+    const uint32_t kc2 = keep_cmp_const(a.drop_T);
+    float m_run = kNegInf;   // running row maximum (log2 units of scaled scores)
+    float l_run = 0.f;       // running normaliser, this lane's half of the keys
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    f32x16 s;                // scores of the tile the vector phase works on next
+    uint32_t pp[8];          // rounded (kept) probabilities of the tile the matrix phase multiplies
+
+    // Vector phase for tile t: scores s -> probabilities pp.
+    auto vec_phase = [&](int t) {
+        if (is_edge(t)) apply_mask(s, t);
+        uint32_t keep = 0;
+        if (DROPOUT) {
+            const uint32_t grp = (uint32_t)((klo + t * BC) >> 3) + 2 * (uint32_t)g;
+            const Philox4 b0 = philox4x32_10(grp, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
+            const Philox4 b1 = philox4x32_10(grp + 1, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
+            keep = keep_signs_from_blocks(b0, b1, kc2);
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+        // Move the reference maximum when the tile exceeds it by the threshold.
+        if (__builtin_expect(__ballot(mx * sl2 > m_run + kPPRescaleLog2) != 0, 0)) {
+            const float m_new = fmaxf(m_run, max_halves(mx) * sl2);
+            const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
+            l_run *= alpha;
+            // One block at a time, back into the accumulation registers
+            // (the accumulators live there; a whole-tile multiply would pull
+            // all of them into vector registers).
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                f32x16 x = o[db];
+                pin_vgpr(x);   // explicit copy out of the accumulation registers
+                x *= alpha;
+                pin_agpr(x);   // and back
+                o[db] = x;
+            }
+            m_run = m_new;
+        }
+        const float mu = m_run == kNegInf ? 0.f : m_run;
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p0 = fast_exp2(fmaf(s[2 * i], sl2, -mu));
+            const float p1 = fast_exp2(fmaf(s[2 * i + 1], sl2, -mu));
+            // row sums keep the dropped probabilities
+            if (i & 1) acc1 = (acc1 + p0) + p1;
+            else acc0 = (acc0 + p0) + p1;
+            pp[i] = pack2<T>(p0, p1);
+            if (DROPOUT) {
+                // decisions of pair i in the sign bits of the two halves
+                const i16x2 sg = __builtin_bit_cast(i16x2, keep << i);
+                pp[i] &= __builtin_bit_cast(uint32_t, sg >> (i16x2){15, 15});
+            }
+        }
+        l_run += acc0 + acc1;
+    };
+
+    // Matrix phase of tile t (parity P): O^T += V^T P^T (V_t, pp) and S of
+    // tile t + 1 (K_{t+1}) into s.  The last tile's phase also forms the
+    // scores of the tile after it, which are never used: every phase has one
+    // shape.  The S chain and the O products alternate, so no product waits
+    // for the one just issued; fragments are read two product pairs ahead.
+    auto mat_phase = [&](auto par_c) {
+        constexpr int P = decltype(par_c)::value;
+        const lds_char *kb = P ? (lds_char *)ks0 : (lds_char *)ks1;   // K_{t+1}
+        const lds_char *vb = P ? (lds_char *)vs1 : (lds_char *)vs0;   // V_t
+        auto kfrag = [&](int j) { return lds_frag<T>(kb + koff[j]); };
+        auto vfrag = [&](int j) {
+            const int cc = j / NDB, db = j % NDB;
+            const uint32_t kc_off = (uint32_t)(16 * cc * RB);
+            return join<T>(lds_half_tr<T>(vb + kc_off + voff[0][db]),
+                           lds_half_tr<T>(vb + kc_off + voff[1][db]));
+        };
+        auto pfrag = [&](int cc) {
+            u32x4 pv;
+            pv[0] = pp[4 * cc + 0];
+            pv[1] = pp[4 * cc + 1];
+            pv[2] = pp[4 * cc + 2];
+            pv[3] = pp[4 * cc + 3];
+            return __builtin_bit_cast(frag_t<T>, pv);
+        };
+        __builtin_amdgcn_s_setprio(1);
+        s = f32x16{};
+        frag_t<T> kf[3], vf[3];
+        kf[0] = kfrag(0);
+        vf[0] = vfrag(0);
+        kf[1] = kfrag(1);
+        vf[1] = vfrag(1);
+#pragma unroll
+        for (int j = 0; j < NDC; ++j) {
+            if (j + 2 < NDC) {
+                kf[(j + 2) % 3] = kfrag(j + 2);
+                vf[(j + 2) % 3] = vfrag(j + 2);
+            }
+            mma(s, kf[j % 3], qf[j]);
+            mma(o[j % NDB], vf[j % 3], pfrag(j / NDB));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // End of step t: this wavefront's loads landed, then everyone's (the
+    // buffers of K_{t+1} and V_t are free); then the loads of step t + 1,
+    // K_{t+3} and V_{t+2}, into them.
+    auto end_step = [&](int t) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 2 < NT) load_step(t + 3, t + 2);
+    };
+
+    // ---- prologue: K_0, K_1 and V_0; S of tile 0; then step 0's loads
+    // (K_2 into the buffer of K_0, V_1).
+    load_step(0, 0);
+    load_step(1, 0);   // (V_0 loaded twice: same data, same place)
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) pin_agpr(qf[c]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (Tw > 0) {
+        s = f32x16{};
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) mma(s, lds_frag<T>((lds_char *)ks0 + koff[c]), qf[c]);
+    }
+    __syncthreads();   // K buffer 0 is refilled in step 0
+    if (NT > 1) load_step(2, 1);
+
+    // ---- steps.  Both halves run the phase sequence vec(0) mat(0) vec(1)
+    // mat(1) ... mat(Tw-1); step t (one barrier) is [vec(t) mat(t)] for the
+    // second half and [mat(t) vec(t+1)] for the first, so the two
+    // wavefronts of a SIMD are in opposite phases.  Step t reads K_{t+1} and
+    // V_t in both.  Two steps per trip, so buffer parities are constants.
+    // Wavefronts past their last tile keep the loads and barriers of the
+    // workgroup going.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto step = [&](auto par_c, int t) {
+        vec_phase(t);
+        if (order == 0 && t > 0) end_step(t - 1);
+        mat_phase(par_c);
+        if (order != 0) end_step(t);
+    };
+    for (int t = 0; t < Tw; t += 2) {
+        step(I0{}, t);
+        if (t + 1 < Tw) step(I1{}, t + 1);
+    }
+    if (order == 0 && Tw > 0) end_step(Tw - 1);
+    for (int t = Tw; t < NT; ++t) end_step(t);
+
+    // ---- epilogue: O = c acc / l, LSE = (m + log2 l) ln 2 (of the chunk,
+    // in fp32 to the partial buffers, when the keys are split).
+    const bool part = a.kv_splits > 1;
+    const size_t prow = ((size_t)split * (size_t)BH + (size_t)bh) * (size_t)N;
+    const float l_tot = sum_halves(l_run);
+    const float inv = l_tot > 0.f ? (DROPOUT ? a.drop_c : 1.f) / l_tot : 0.f;
+    if (qrow < N) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int col = 32 * db + 8 * rr + 4 * g;
+                const float x0 = o[db][4 * rr + 0] * inv, x1 = o[db][4 * rr + 1] * inv;
+                const float x2 = o[db][4 * rr + 2] * inv, x3 = o[db][4 * rr + 3] * inv;
+                if (part) {
+                    store4<float>(a.part_o + (prow + qrow) * D + col, x0, x1, x2, x3);
+                } else if (a.out_f32) {
+                    float *O = reinterpret_cast<float *>(a.o) + head;
+                    store4<float>(O + (size_t)qrow * D + col, x0, x1, x2, x3);
+                } else {
+                    T *O = reinterpret_cast<T *>(a.o) + head;
+                    store4<T>(O + (size_t)qrow * D + col, x0, x1, x2, x3);
+                }
+            }
+        if (g == 0) {
+            const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : kNegInf;
+            if (part) a.part_lse[prow + qrow] = lse;
+            else a.lse[(size_t)bh * (size_t)N + qrow] = lse;
+        }
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, hipStream_t stream) {
+    using TL = FwdPPTile<T, D>;
+    const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
+    const int64_t units = a.B * a.H * nqb * a.kv_splits;
+    if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)units), block(TL::THREADS);
+    if (causal) {
+        if (dropout) hipLaunchKernelGGL((fwd_pp_kernel<T, D, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((fwd_pp_kernel<T, D, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (dropout) hipLaunchKernelGGL((fwd_pp_kernel<T, D, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((fwd_pp_kernel<T, D, false, false>), grid, block, 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
+                         hipStream_t stream) {
+    if (d != 128) return hipErrorInvalidValue;
+    if (e == Elem::BF16) return launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream);
+    if (e == Elem::F16) return launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -56,6 +56,9 @@ hipError_t launch_bwd_dq16(Elem e, int d, bool causal, bool dropout, const BwdAr
                            hipStream_t stream);
 hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                              hipStream_t stream);
+// 16-bit inputs at d = 128: eight wavefronts per workgroup, two per SIMD.
+hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
+                         hipStream_t stream);
 // Combines the kv_splits partial results of a split forward into o and lse.
 hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream);
 hipError_t launch_dropout_mask(int64_t N, uint32_t T, uint32_t seed_lo, uint32_t seed_hi,
