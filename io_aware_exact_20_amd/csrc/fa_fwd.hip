@@ -29,7 +29,7 @@
 #include "fa_kernels.hpp"
 
 #ifndef FA_FWD_KH0
-#define FA_FWD_KH0 (2 * SB)
+#define FA_FWD_KH0 (2 * SB + SC)   // generator rounds over the second half of the PV products
 #endif
 
 #ifndef FA_FWD_PP
