@@ -35,11 +35,16 @@
 
 namespace fa {
 
-template <typename T, int D>
+template <typename T, int D, bool DROPOUT>
 struct FwdPPTile {
     static constexpr int NW = 8;                          // wavefronts, two per SIMD
     static constexpr int BQ = 32 * NW;                    // query rows per workgroup
-    static constexpr int BC = 32;                         // keys per tile
+    // 32-key blocks per tile: two (one barrier per 64 keys) unless the
+    // keep-mask generator's registers do not leave room for them.
+    static constexpr int NKB = DROPOUT ? 1 : 2;
+    // K and V buffers each; tiles are loaded NBUF - 1 steps ahead.
+    static constexpr int NBUF = DROPOUT ? 2 : 3;
+    static constexpr int BC = 32 * NKB;                   // keys per tile
     static constexpr int THREADS = NW * kWave;
     static constexpr int TILE_BYTES = BC * D * 2;         // one K or V tile
     static constexpr int CHUNK_BYTES = kWave * 16;        // one wavefront load instruction
@@ -52,9 +57,9 @@ constexpr float kPPRescaleLog2 = 8.0f;
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>
 __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
-    using TL = FwdPPTile<T, D>;
+    using TL = FwdPPTile<T, D, DROPOUT>;
     using SW = Swz<D>;
-    constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW;
+    constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW, NKB = TL::NKB, NBUF = TL::NBUF;
     constexpr int TB = TL::TILE_BYTES, CB = TL::CHUNK_BYTES, CHUNKS = TL::CHUNKS, LOADS = TL::LOADS;
     constexpr int RB = SW::ROW_BYTES;
     constexpr int RPC = CB / RB;      // tile rows per load instruction
@@ -62,11 +67,12 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
     constexpr int NDB = D / 32;       // 32-column blocks of O
     constexpr float kNegInf = -__builtin_huge_valf();
     static_assert(D == 128, "tile plan for d = 128");
-    static_assert(2 * CHUNKS == LOADS * NW && LOADS >= 1, "load split");
     static_assert(2 * NDB == NDC, "one V^T product per K product");
 
-    // LDS: K tile t in buffer t & 1, V tile t in buffer t & 1.
+    // LDS: K tile t in buffer t % NBUF, V tile t in buffer t % NBUF (the
+    // third buffers are unused when NBUF = 2).
     __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], vs0[TB], vs1[TB];
+    __shared__ __attribute__((aligned(1024))) char ks2[NBUF > 2 ? TB : 16], vs2[NBUF > 2 ? TB : 16];
 
     const int lane = (int)lane_in_wave();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -118,34 +124,33 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
                 voff[hf][db] = SW::off(8 * hf + 4 * (G >> 1) + k, 32 * db + 16 * (G & 1) + 4 * j);
     }
 
-    // Tile loads.  Load instruction L (0 .. 2 CHUNKS - 1) of a step fills
-    // rows RPC (L % CHUNKS) .. of the K (L < CHUNKS) or V tile; this
-    // wavefront issues L = wave + i NW.  Lane l loads the logical 16-byte
+    // Tile loads.  A tile is CHUNKS load instructions of 1 KB (RPC rows
+    // each); this wavefront issues chunks c = wave + i NW (i < LPT) of both
+    // the K and the V tile of a step.  Lane l loads the logical 16-byte
     // chunk that the swizzle places at position l % CPR of its row.
-    uint32_t lboff[LOADS];
+    constexpr int LPT = CHUNKS / NW;   // chunks per tile per wavefront
+    static_assert(LPT * NW == CHUNKS && 2 * LPT == LOADS, "load split");
+    uint32_t lboff[LPT];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int L = wave + i * NW;
-        const int r = RPC * (L % CHUNKS) + lane / SW::CPR;
+    for (int i = 0; i < LPT; ++i) {
+        const int r = RPC * (wave + i * NW) + lane / SW::CPR;
         lboff[i] = ((uint32_t)r * D + (uint32_t)(((lane % SW::CPR) ^ (int)SW::f((uint32_t)r)) * 8)) * 2;
     }
     const uint32_t head_bytes = (uint32_t)Nk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
-    // Buffers by parity (compile-time wherever tiles are read, so that the
-    // compiler can tell the loads into one buffer from reads of the other).
-    auto kbuf = [&](int par) { return par ? (lds_char *)ks1 : (lds_char *)ks0; };
-    auto vbuf = [&](int par) { return par ? (lds_char *)vs1 : (lds_char *)vs0; };
-    // This wavefront's share of the loads of K tile tk and V tile tv (into
-    // the buffers of their parities).
-    auto load_step = [&](int tk, int tv) {
+    // Buffers by tile index mod 3 (compile-time wherever tiles are read, so
+    // that the compiler can tell the loads into one buffer from reads of
+    // another).
+    auto kbuf = [&](int m) { return m == 0 ? (lds_char *)ks0 : m == 1 ? (lds_char *)ks1 : (lds_char *)ks2; };
+    auto vbuf = [&](int m) { return m == 0 ? (lds_char *)vs0 : m == 1 ? (lds_char *)vs1 : (lds_char *)vs2; };
+    // This wavefront's share of the loads of K tile tk and V tile tv into
+    // K buffer kbm and V buffer vbm.
+    auto load_kv = [&](int tk, int kbm, int tv, int vbm) {
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int L = wave + i * NW;
-            const int c = L % CHUNKS;
-            if (L < CHUNKS)
-                buf2lds16(krs, lboff[i], (uint32_t)((klo + tk * BC) * D * 2), kbuf(tk & 1) + c * CB);
-            else
-                buf2lds16(vrs, lboff[i], (uint32_t)((klo + tv * BC) * D * 2), vbuf(tv & 1) + c * CB);
+        for (int i = 0; i < LPT; ++i) {
+            const int c = wave + i * NW;
+            buf2lds16(krs, lboff[i], (uint32_t)((klo + tk * BC) * D * 2), kbuf(kbm) + c * CB);
+            buf2lds16(vrs, lboff[i], (uint32_t)((klo + tv * BC) * D * 2), vbuf(vbm) + c * CB);
         }
     };
 
@@ -162,10 +167,11 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
         const int64_t k0 = (int64_t)klo + t * BC;
         return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + off);
     };
-    // Register r holds key k0 + 4g + kk(r), kk(r) = 8(r/4) + r%4, for query
-    // row qrow; masked: key >= Nk, or (causal) key > qrow + off.
-    auto apply_mask = [&](f32x16 &s, int t) {
-        const int k0 = klo + t * BC;
+    // Register r of key block kb holds key k0 + 4g + kk(r), k0 = first key
+    // of the block, kk(r) = 8(r/4) + r%4, for query row qrow; masked: key >=
+    // Nk, or (causal) key > qrow + off.
+    auto apply_mask = [&](f32x16 &s, int t, int kb) {
+        const int k0 = klo + t * BC + 32 * kb;
         int lim = Nk - 1 - (k0 + 4 * g);
         if (CAUSAL) {
             const int64_t c = (int64_t)qrow + off - (k0 + 4 * g);
@@ -185,22 +191,33 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    f32x16 s;                // scores of the tile the vector phase works on next
-    uint32_t pp[8];          // rounded (kept) probabilities of the tile the matrix phase multiplies
+    f32x16 s[NKB];           // scores of the tile the vector phase works on next
+    uint32_t pp[8 * NKB];    // rounded (kept) probabilities of the tile the matrix phase multiplies
 
     // Vector phase for tile t: scores s -> probabilities pp.
     auto vec_phase = [&](int t) {
-        if (is_edge(t)) apply_mask(s, t);
-        uint32_t keep = 0;
-        if (DROPOUT) {
-            const uint32_t grp = (uint32_t)((klo + t * BC) >> 3) + 2 * (uint32_t)g;
-            const Philox4 b0 = philox4x32_10(grp, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
-            const Philox4 b1 = philox4x32_10(grp + 1, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
-            keep = keep_signs_from_blocks(b0, b1, kc2);
+        if (is_edge(t)) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) apply_mask(s[kb], t, kb);
+        }
+        // Keep decisions of each 32-key block, in the sign layout (drawn
+        // before the scores are read into vector registers).
+        uint32_t keep_blk[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            keep_blk[kb] = 0;
+            if (DROPOUT) {
+                const uint32_t grp = (uint32_t)((klo + t * BC + 32 * kb) >> 3) + 2 * (uint32_t)g;
+                const Philox4 b0 = philox4x32_10(grp, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
+                const Philox4 b1 = philox4x32_10(grp + 1, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
+                keep_blk[kb] = keep_signs_from_blocks(b0, b1, kc2);
+            }
         }
         float mx = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
         // Move the reference maximum when the tile exceeds it by the threshold.
         if (__builtin_expect(__ballot(mx * sl2 > m_run + kPPRescaleLog2) != 0, 0)) {
             const float m_new = fmaxf(m_run, max_halves(mx) * sl2);
@@ -222,32 +239,41 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
         const float mu = m_run == kNegInf ? 0.f : m_run;
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p0 = fast_exp2(fmaf(s[2 * i], sl2, -mu));
-            const float p1 = fast_exp2(fmaf(s[2 * i + 1], sl2, -mu));
-            // row sums keep the dropped probabilities
-            if (i & 1) acc1 = (acc1 + p0) + p1;
-            else acc0 = (acc0 + p0) + p1;
-            pp[i] = pack2<T>(p0, p1);
-            if (DROPOUT) {
-                // decisions of pair i in the sign bits of the two halves
-                const i16x2 sg = __builtin_bit_cast(i16x2, keep << i);
-                pp[i] &= __builtin_bit_cast(uint32_t, sg >> (i16x2){15, 15});
+        for (int kb = 0; kb < NKB; ++kb) {
+            const uint32_t keep = keep_blk[kb];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = fast_exp2(fmaf(s[kb][2 * i], sl2, -mu));
+                const float p1 = fast_exp2(fmaf(s[kb][2 * i + 1], sl2, -mu));
+                // row sums keep the dropped probabilities
+                if (i & 1) acc1 = (acc1 + p0) + p1;
+                else acc0 = (acc0 + p0) + p1;
+                uint32_t w = pack2<T>(p0, p1);
+                if (DROPOUT) {
+                    // decisions of pair i in the sign bits of the two halves
+                    const i16x2 sg = __builtin_bit_cast(i16x2, keep << i);
+                    w &= __builtin_bit_cast(uint32_t, sg >> (i16x2){15, 15});
+                }
+                pp[8 * kb + i] = w;
             }
         }
         l_run += acc0 + acc1;
     };
 
-    // Matrix phase of tile t (parity P): O^T += V^T P^T (V_t, pp) and S of
+    // Matrix phase of tile t (M = t % NBUF): O^T += V^T P^T (V_t, pp) and S of
     // tile t + 1 (K_{t+1}) into s.  The last tile's phase also forms the
     // scores of the tile after it, which are never used: every phase has one
     // shape.  The S chain and the O products alternate, so no product waits
     // for the one just issued; fragments are read two product pairs ahead.
-    auto mat_phase = [&](auto par_c) {
-        constexpr int P = decltype(par_c)::value;
-        const lds_char *kb = P ? (lds_char *)ks0 : (lds_char *)ks1;   // K_{t+1}
-        const lds_char *vb = P ? (lds_char *)vs1 : (lds_char *)vs0;   // V_t
-        auto kfrag = [&](int j) { return lds_frag<T>(kb + koff[j]); };
+    auto mat_phase = [&](auto m_c) {
+        constexpr int M = decltype(m_c)::value;
+        constexpr int NJ = NKB * NDC;   // products of each kind (S: key block x d chunk; O: key chunk x d block)
+        constexpr int MK = (M + 1) % NBUF;
+        const lds_char *kb_ = MK == 0 ? (lds_char *)ks0 : MK == 1 ? (lds_char *)ks1 : (lds_char *)ks2;  // K_{t+1}
+        const lds_char *vb = M == 0 ? (lds_char *)vs0 : M == 1 ? (lds_char *)vs1 : (lds_char *)vs2;      // V_t
+        // S product j: key block j / NDC, contraction chunk j % NDC.
+        auto kfrag = [&](int j) { return lds_frag<T>(kb_ + (j / NDC) * 32 * RB + koff[j % NDC]); };
+        // O product j: key chunk (16 keys) j / NDB, output block j % NDB.
         auto vfrag = [&](int j) {
             const int cc = j / NDB, db = j % NDB;
             const uint32_t kc_off = (uint32_t)(16 * cc * RB);
@@ -263,71 +289,99 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
             return __builtin_bit_cast(frag_t<T>, pv);
         };
         __builtin_amdgcn_s_setprio(1);
-        s = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
         frag_t<T> kf[3], vf[3];
         kf[0] = kfrag(0);
         vf[0] = vfrag(0);
         kf[1] = kfrag(1);
         vf[1] = vfrag(1);
 #pragma unroll
-        for (int j = 0; j < NDC; ++j) {
-            if (j + 2 < NDC) {
+        for (int j = 0; j < NJ; ++j) {
+            if (j + 2 < NJ) {
                 kf[(j + 2) % 3] = kfrag(j + 2);
                 vf[(j + 2) % 3] = vfrag(j + 2);
             }
-            mma(s, kf[j % 3], qf[j]);
+            mma(s[j / NDC], kf[j % 3], qf[j % NDC]);
             mma(o[j % NDB], vf[j % 3], pfrag(j / NDB));
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // End of step t: this wavefront's loads landed, then everyone's (the
-    // buffers of K_{t+1} and V_t are free); then the loads of step t + 1,
-    // K_{t+3} and V_{t+2}, into them.
-    auto end_step = [&](int t) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (t + 2 < NT) load_step(t + 3, t + 2);
+    // Loads run two steps ahead: step t brings K_{t+3} and V_{t+2} (into
+    // the buffers of K_t and V_{t-1}, free since the end of step t-1), and
+    // the end of step t waits only for the loads of step t-1 (K_{t+2},
+    // V_{t+1}, which step t+1 reads); this step's LOADS loads stay in
+    // flight across the barrier.  Loads past the end read zeros (or keys
+    // no row uses), so every step issues the same number and the count is
+    // exact.  The barrier is the bare instruction after explicit counts (a
+    // workgroup fence would wait for every load in flight); no memory
+    // operation is moved across it (scheduling barriers on both sides, and
+    // the hardware barrier is an unmodelled side effect for the compiler).
+    // (The buffer indices of the loads are compile-time constants too, so
+    // that the compiler sees which buffer each direct load writes.)
+    auto end_step = [&](auto m_c, int t) {   // m_c: t % NBUF
+        constexpr int M = decltype(m_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        // vmcnt(LOADS (NBUF - 2)), lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0070 | (LOADS * (NBUF - 2)));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        load_kv(t + 1 + NBUF, (M + 1) % NBUF, t + NBUF, M);   // K_{t+1+NBUF}, V_{t+NBUF}
     };
-
-    // ---- prologue: K_0, K_1 and V_0; S of tile 0; then step 0's loads
-    // (K_2 into the buffer of K_0, V_1).
-    load_step(0, 0);
-    load_step(1, 0);   // (V_0 loaded twice: same data, same place)
+    // ---- prologue: K_0, K_1, V_0, then S of tile 0; then the loads of the
+    // steps before step 0 and of step 0 itself (K_2, V_1, and with three
+    // buffers K_3, V_2).
+    load_kv(0, 0, 0, 0);
+    load_kv(1, 1, 0, 0);   // (V_0 loaded twice: same data, same place)
 #pragma unroll
     for (int c = 0; c < NDC; ++c) pin_agpr(qf[c]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (Tw > 0) {
-        s = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) mma(s, lds_frag<T>((lds_char *)ks0 + koff[c]), qf[c]);
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < NDC; ++c) mma(s[kb], lds_frag<T>((lds_char *)ks0 + kb * 32 * RB + koff[c]), qf[c]);
+        }
     }
-    __syncthreads();   // K buffer 0 is refilled in step 0
-    if (NT > 1) load_step(2, 1);
+    __syncthreads();   // K buffer 0 is refilled before step 0
+#pragma unroll
+    for (int u = 2; u <= NBUF; ++u) load_kv(u, u % NBUF, u - 1, (u - 1) % NBUF);   // K_u, V_{u-1}
 
     // ---- steps.  Both halves run the phase sequence vec(0) mat(0) vec(1)
     // mat(1) ... mat(Tw-1); step t (one barrier) is [vec(t) mat(t)] for the
     // second half and [mat(t) vec(t+1)] for the first, so the two
     // wavefronts of a SIMD are in opposite phases.  Step t reads K_{t+1} and
-    // V_t in both.  Two steps per trip, so buffer parities are constants.
+    // V_t in both.  Three steps per trip, so buffer indices are constants.
     // Wavefronts past their last tile keep the loads and barriers of the
     // workgroup going.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    auto step = [&](auto par_c, int t) {
+    using I2 = std::integral_constant<int, 2>;
+    auto step = [&](auto m_c, int t) {
+        constexpr int M = decltype(m_c)::value;
         vec_phase(t);
-        if (order == 0 && t > 0) end_step(t - 1);
-        mat_phase(par_c);
-        if (order != 0) end_step(t);
+        if (order == 0 && t > 0) end_step(std::integral_constant<int, (M + NBUF - 1) % NBUF>{}, t - 1);
+        mat_phase(m_c);
+        if (order != 0) end_step(m_c, t);
     };
-    for (int t = 0; t < Tw; t += 2) {
+    auto end_step_rt = [&](int t) {   // run-time t % NBUF (no LDS reads follow)
+        const int m = t % NBUF;
+        if (m == 0) end_step(I0{}, t);
+        else if (m == 1) end_step(I1{}, t);
+        else end_step(std::integral_constant<int, (NBUF > 2 ? 2 : 1)>{}, t);
+    };
+    for (int t = 0; t < Tw; t += NBUF) {
         step(I0{}, t);
         if (t + 1 < Tw) step(I1{}, t + 1);
+        if (NBUF > 2 && t + 2 < Tw) step(std::integral_constant<int, (NBUF > 2 ? 2 : 0)>{}, t + 2);
     }
-    if (order == 0 && Tw > 0) end_step(Tw - 1);
-    for (int t = Tw; t < NT; ++t) end_step(t);
+    if (order == 0 && Tw > 0) end_step_rt(Tw - 1);
+    for (int t = Tw; t < NT; ++t) end_step_rt(t);
+    __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the workgroup
 
     // ---- epilogue: O = c acc / l, LSE = (m + log2 l) ln 2 (of the chunk,
     // in fp32 to the partial buffers, when the keys are split).
@@ -363,7 +417,7 @@ __global__ void __launch_bounds__(512, 1) fwd_pp_kernel(const FwdArgs a) {
 
 template <typename T, int D>
 static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, hipStream_t stream) {
-    using TL = FwdPPTile<T, D>;
+    using TL = FwdPPTile<T, D, false>;   // BQ does not depend on dropout
     const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
     const int64_t units = a.B * a.H * nqb * a.kv_splits;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
