@@ -171,7 +171,9 @@ __global__ void __launch_bounds__(kPPThreads<DROPOUT>, kPPWgPerCu<DROPOUT>) fwd_
         return end > klo ? (int)((end - klo + BC - 1) / BC) : 0;
     };
     const int NT = tiles_to(CAUSAL ? (int64_t)q0 + BQ + off : (int64_t)Nk);   // workgroup
-    const int Tw = tiles_to(CAUSAL ? (int64_t)q0w + 32 + off : (int64_t)Nk);  // this wavefront
+    // Tiles this wavefront works on (none when all its rows are past the
+    // last query, e.g. the tail of a short decoding block).
+    const int Tw = q0w < N ? tiles_to(CAUSAL ? (int64_t)q0w + 32 + off : (int64_t)Nk) : 0;
 
     // Tile t needs masking if it reaches past the last key or, causal, past
     // what the wavefront's first row sees.

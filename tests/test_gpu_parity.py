@@ -172,6 +172,9 @@ CROSS = [
     ("bf16", 64, 77, 4096, False, 0.1), ("f16", 128, 130, 555, True, 0.0),
     ("bf16", 96, 50, 333, True, 0.1), ("bf16", 256, 40, 300, True, 0.0),
     ("f32", 64, 77, 200, True, 0.1), ("f32", 128, 33, 64, False, 0.0),
+    # d = 128 with fewer keys than queries: whole wavefronts of rows see no key
+    ("bf16", 128, 1000, 300, True, 0.1), ("bf16", 128, 700, 250, True, 0.0),
+    ("f16", 128, 600, 100, True, 0.1),
 ]
 
 
