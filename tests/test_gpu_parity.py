@@ -349,8 +349,11 @@ def test_long_context_65536_sampled_rows(gpu_lib):
 
 @pytest.mark.parametrize("N", [1, 2, 63, 65, 127, 129, 1000])
 @pytest.mark.parametrize("causal", [False, True])
-def test_ragged_lengths(gpu_lib, N, causal):
-    w = Workload("ragged", 1, 2, N, 128, "bf16", causal=causal, dropout_p=0.2, backward=True,
+@pytest.mark.parametrize("p", [0.0, 0.2])
+def test_ragged_lengths(gpu_lib, N, causal, p):
+    """Sequence lengths around the tile sizes (32-key steps with dropout,
+    64-key steps without it at d = 128)."""
+    w = Workload("ragged", 1, 2, N, 128, "bf16", causal=causal, dropout_p=p, backward=True,
                  seed=N, dropout_seed=N * 31 + 7)
     q, k, v, do = workloads.draw(w)
     o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
@@ -360,11 +363,11 @@ def test_ragged_lengths(gpu_lib, N, causal):
         compare(name, got, exact, w.dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_single_key_returns_value_exactly(gpu_lib, dtype):
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 64), ("bf16", 128), ("f16", 128)])
+def test_single_key_returns_value_exactly(gpu_lib, dtype, d):
     """N = 1: exp(0) = 1 and l = 1, so O must equal V bit for bit and
     LSE = scale q.k; dV = dO bit for bit and dQ = dK = 0 (to rounding)."""
-    w = Workload("n1", 3, 4, 1, 64, dtype, causal=True, backward=True, seed=99)
+    w = Workload("n1", 3, 4, 1, d, dtype, causal=True, backward=True, seed=99)
     q, k, v, do = workloads.draw(w)
     o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
     assert torch.equal(o.cpu(), v)
