@@ -47,8 +47,9 @@ struct FwdPPTile {
     static constexpr int NW = DROPOUT ? 4 : 8;
     static constexpr int WG_PER_CU = DROPOUT ? 2 : 1;
     static constexpr int BQ = 32 * NW;                    // query rows per workgroup
-    // 32-key blocks per tile: two (one barrier per 64 keys) unless the
-    // keep-mask generator's registers do not leave room for them.
+    // 32-key blocks per tile: two without dropout (one barrier per 64 keys);
+    // one with it (two measured no faster there and need the vector phase
+    // inlined by force to stay out of scratch memory).
     static constexpr int NKB = DROPOUT ? 1 : 2;
     // K and V buffers each; tiles are loaded NBUF - 1 steps ahead.
     static constexpr int NBUF = DROPOUT ? 2 : 3;
