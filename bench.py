@@ -281,7 +281,7 @@ def main():
         torch.cuda.empty_cache()
         # The training shape at the other head dimensions (generic kernels).
         hd = {}
-        for d in (32, 96, 256):
+        for d in (32, 64, 96, 256):
             wd = workloads.WORKLOADS["train_d%d" % d]
             pd = make_problem(fa, wd, dev)
             walld, perd = time_steps(pd, 3, 1)

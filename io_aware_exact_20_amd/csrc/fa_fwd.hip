@@ -872,14 +872,16 @@ hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream)
 
 hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                       hipStream_t stream) {
-    // 16-bit inputs: d = 128 takes the two-wavefronts-per-SIMD kernel
-    // (fa_fwd_pp.hip), d = 64 the 64-rows-per-wavefront kernel; every other
-    // case the generic one (32 rows per wavefront).
+    // 16-bit inputs: d = 64 and 128 take the two-wavefronts-per-SIMD kernel
+    // (fa_fwd_pp.hip; the 64-rows-per-wavefront kernel when built with
+    // FA_FWD_PP=0); every other case the generic one (32 rows per wavefront).
     switch (e) {
     case Elem::BF16:
         switch (d) {
         case 32: return launch_fwd_t<bf16, 32>(causal, dropout, a, stream);
-        case 64: return launch_fwd16_t<bf16, 64, FA_FWD_NW>(causal, dropout, a, stream);
+        case 64:
+            if (FA_FWD_PP) return launch_fwd_pp(e, d, causal, dropout, a, stream);
+            return launch_fwd16_t<bf16, 64, FA_FWD_NW>(causal, dropout, a, stream);
         case 96: return launch_fwd_t<bf16, 96>(causal, dropout, a, stream);
         case 128:
             if (FA_FWD_PP) return launch_fwd_pp(e, d, causal, dropout, a, stream);
@@ -890,7 +892,9 @@ hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a
     case Elem::F16:
         switch (d) {
         case 32: return launch_fwd_t<f16, 32>(causal, dropout, a, stream);
-        case 64: return launch_fwd16_t<f16, 64, FA_FWD_NW>(causal, dropout, a, stream);
+        case 64:
+            if (FA_FWD_PP) return launch_fwd_pp(e, d, causal, dropout, a, stream);
+            return launch_fwd16_t<f16, 64, FA_FWD_NW>(causal, dropout, a, stream);
         case 96: return launch_fwd_t<f16, 96>(causal, dropout, a, stream);
         case 128:
             if (FA_FWD_PP) return launch_fwd_pp(e, d, causal, dropout, a, stream);

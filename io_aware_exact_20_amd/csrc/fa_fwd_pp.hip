@@ -1,5 +1,5 @@
-// Forward of fused exact attention for 16-bit inputs at d = 128 on gfx950,
-// with two wavefronts per SIMD working in opposite phases.
+// Forward of fused exact attention for 16-bit inputs at d = 64 and 128 on
+// gfx950, with two wavefronts per SIMD.
 //
 // The method is the one of the other forward kernels: Q, K, V tiled into
 // on-chip blocks, the online-softmax recurrence (running row maximum,
@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(kPPThreads<DROPOUT>, kPPWgPerCu<DROPOUT>) fwd_
     constexpr int NDC = D / 16;       // contraction chunks of S
     constexpr int NDB = D / 32;       // 32-column blocks of O
     constexpr float kNegInf = -__builtin_huge_valf();
-    static_assert(D == 128, "tile plan for d = 128");
+    static_assert(D == 64 || D == 128, "tile plan for d = 64 and 128");
     static_assert(2 * NDB == NDC, "one V^T product per K product");
 
     // LDS: K tile t in buffer t % NBUF, V tile t in buffer t % NBUF (the
@@ -449,9 +449,13 @@ static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, h
 
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                          hipStream_t stream) {
-    if (d != 128) return hipErrorInvalidValue;
-    if (e == Elem::BF16) return launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream);
-    if (e == Elem::F16) return launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream);
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
+    if (e == Elem::BF16)
+        return d == 64 ? launch_fwd_pp_t<bf16, 64>(causal, dropout, a, stream)
+                       : launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream);
+    if (e == Elem::F16)
+        return d == 64 ? launch_fwd_pp_t<f16, 64>(causal, dropout, a, stream)
+                       : launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream);
     return hipErrorInvalidValue;
 }
 
