@@ -21,7 +21,7 @@
 // Without dropout a workgroup has eight wavefronts (256 rows, 64-key
 // steps): wavefronts 0-3 run matrix then vector phase, 4-7 vector then
 // matrix phase, and the two wavefronts on one SIMD (w and w + 4) belong to
-// different halves.  With dropout a workgroup has four wavefronts (128
+// different halves (and own row blocks w and 7 - w).  With dropout a workgroup has four wavefronts (128
 // rows, 32-key steps) and two workgroups share a CU, so the other
 // workgroup's wavefronts run while one waits at its step barrier.
 
@@ -90,9 +90,11 @@ __global__ void __launch_bounds__(kPPThreads<DROPOUT>, kPPWgPerCu<DROPOUT>) fwd_
     const int lane = (int)lane_in_wave();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lq = lane & 31, g = lane >> 5;
-    // Wavefronts w and w + 4 share a SIMD and own adjacent 32-row blocks.
     const int order = NW == 8 ? wave >> 2 : 0;       // 0: matrix phase first
-    const int rblk = NW == 8 ? 2 * (wave & 3) + order : wave;
+    // Eight wavefronts: waves w and w + 4 share a SIMD and own row blocks w
+    // and 7 - w, so that on the causal diagonal every SIMD pairs a long and
+    // a short wavefront (the long one has the SIMD to itself at the end).
+    const int rblk = NW == 8 ? (order == 0 ? (wave & 3) : 7 - (wave & 3)) : wave;
 
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
