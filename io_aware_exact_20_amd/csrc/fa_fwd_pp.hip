@@ -326,13 +326,13 @@ __global__ void __launch_bounds__(kPPThreads<DROPOUT>, kPPWgPerCu<DROPOUT>) fwd_
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // Loads run two steps ahead: step t brings K_{t+3} and V_{t+2} (into
-    // the buffers of K_t and V_{t-1}, free since the end of step t-1), and
-    // the end of step t waits only for the loads of step t-1 (K_{t+2},
-    // V_{t+1}, which step t+1 reads); this step's LOADS loads stay in
-    // flight across the barrier.  Loads past the end read zeros (or keys
-    // no row uses), so every step issues the same number and the count is
-    // exact.  The barrier is the bare instruction after explicit counts (a
+    // Loads run NBUF - 1 steps ahead: step t brings K_{t+NBUF} and
+    // V_{t+NBUF-1} (into the buffers of K_t and V_{t-1}, free since the end
+    // of step t-1), and the end of step t waits for every load but this
+    // step's own when NBUF = 3 (the loads of step t-1 are K_{t+2}, V_{t+1},
+    // which step t+1 reads), for all of them when NBUF = 2.  Loads past the
+    // end read zeros (or keys no row uses), so every step issues the same
+    // number and the count is exact.  The barrier is the bare instruction after explicit counts (a
     // workgroup fence would wait for every load in flight); no memory
     // operation is moved across it (scheduling barriers on both sides, and
     // the hardware barrier is an unmodelled side effect for the compiler).
