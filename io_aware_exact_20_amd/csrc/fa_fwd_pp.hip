@@ -38,21 +38,24 @@
 
 namespace fa {
 
-template <typename T, int D, bool DROPOUT>
+template <typename T, int D, bool DROPOUT, bool W4>
 struct FwdPPTile {
-    // Without dropout: eight wavefronts, two per SIMD in opposite phases.
-    // With dropout: four wavefronts and two workgroups per CU (the second
+    // W4 = false: eight wavefronts, two per SIMD in opposite phases.
+    // W4 = true: four wavefronts and two workgroups per CU (the second
     // workgroup's wavefronts fill the SIMDs while one workgroup waits at its
-    // step barrier; measured 9 % faster than eight wavefronts there).
-    static constexpr int NW = DROPOUT ? 4 : 8;
-    static constexpr int WG_PER_CU = DROPOUT ? 2 : 1;
+    // step barrier); used with dropout (measured 9 % faster than eight
+    // wavefronts there) and for problems with few query blocks (twice as
+    // many, smaller work units).
+    static constexpr int NW = W4 ? 4 : 8;
+    static constexpr int WG_PER_CU = W4 ? 2 : 1;
     static constexpr int BQ = 32 * NW;                    // query rows per workgroup
     // 32-key blocks per tile: two without dropout (one barrier per 64 keys);
     // one with it (two measured no faster there and need the vector phase
     // inlined by force to stay out of scratch memory).
     static constexpr int NKB = DROPOUT ? 1 : 2;
-    // K and V buffers each; tiles are loaded NBUF - 1 steps ahead.
-    static constexpr int NBUF = DROPOUT ? 2 : 3;
+    // K and V buffers each; tiles are loaded NBUF - 1 steps ahead (two
+    // buffers when two workgroups share the LDS).
+    static constexpr int NBUF = W4 ? 2 : 3;
     static constexpr int BC = 32 * NKB;                   // keys per tile
     static constexpr int THREADS = NW * kWave;
     static constexpr int TILE_BYTES = BC * D * 2;         // one K or V tile
@@ -62,15 +65,15 @@ struct FwdPPTile {
 };
 
 // Launch bounds (single template arguments: the attribute macro splits at commas).
-template <bool DROPOUT> constexpr int kPPThreads = FwdPPTile<bf16, 128, DROPOUT>::THREADS;
-template <bool DROPOUT> constexpr int kPPWgPerCu = FwdPPTile<bf16, 128, DROPOUT>::WG_PER_CU;
+template <bool W4> constexpr int kPPThreads = FwdPPTile<bf16, 128, false, W4>::THREADS;
+template <bool W4> constexpr int kPPWgPerCu = FwdPPTile<bf16, 128, false, W4>::WG_PER_CU;
 
 // Lazy-rescale threshold (log2 units), as in the other forward kernels.
 constexpr float kPPRescaleLog2 = 8.0f;
 
-template <typename T, int D, bool CAUSAL, bool DROPOUT>
-__global__ void __launch_bounds__(kPPThreads<DROPOUT>, kPPWgPerCu<DROPOUT>) fwd_pp_kernel(const FwdArgs a) {
-    using TL = FwdPPTile<T, D, DROPOUT>;
+template <typename T, int D, bool CAUSAL, bool DROPOUT, bool W4>
+__global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(const FwdArgs a) {
+    using TL = FwdPPTile<T, D, DROPOUT, W4>;
     using SW = Swz<D>;
     constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW, NKB = TL::NKB, NBUF = TL::NBUF;
     constexpr int TB = TL::TILE_BYTES, CB = TL::CHUNK_BYTES, CHUNKS = TL::CHUNKS, LOADS = TL::LOADS;
@@ -432,21 +435,31 @@ __global__ void __launch_bounds__(kPPThreads<DROPOUT>, kPPWgPerCu<DROPOUT>) fwd_
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool DROPOUT>
+template <typename T, int D, bool CAUSAL, bool DROPOUT, bool W4>
 static hipError_t launch_fwd_pp_k(const FwdArgs &a, hipStream_t stream) {
-    using TL = FwdPPTile<T, D, DROPOUT>;
+    using TL = FwdPPTile<T, D, DROPOUT, W4>;
     const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
     const int64_t units = a.B * a.H * nqb * a.kv_splits;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
-    hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL, DROPOUT>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL, DROPOUT, W4>), grid, block, 0, stream, a);
     return hipGetLastError();
+}
+
+template <typename T, int D, bool CAUSAL>
+static hipError_t launch_fwd_pp_c(bool dropout, const FwdArgs &a, hipStream_t stream) {
+    if (dropout) return launch_fwd_pp_k<T, D, CAUSAL, true, true>(a, stream);
+    // Without dropout, 256-row units unless that gives fewer than two per
+    // CU (256 CUs), in which case 128-row units, two workgroups per CU.
+    const int64_t units256 = a.B * a.H * ((a.N + 255) / 256) * a.kv_splits;
+    if (units256 < 512) return launch_fwd_pp_k<T, D, CAUSAL, false, true>(a, stream);
+    return launch_fwd_pp_k<T, D, CAUSAL, false, false>(a, stream);
 }
 
 template <typename T, int D>
 static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, hipStream_t stream) {
-    if (causal) return dropout ? launch_fwd_pp_k<T, D, true, true>(a, stream) : launch_fwd_pp_k<T, D, true, false>(a, stream);
-    return dropout ? launch_fwd_pp_k<T, D, false, true>(a, stream) : launch_fwd_pp_k<T, D, false, false>(a, stream);
+    return causal ? launch_fwd_pp_c<T, D, true>(dropout, a, stream)
+                  : launch_fwd_pp_c<T, D, false>(dropout, a, stream);
 }
 
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
