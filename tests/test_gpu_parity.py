@@ -322,6 +322,23 @@ def test_long_context_forward_sampled_heads(gpu_lib, name):
         compare("LSE", lse[b, h], elx[b, h], w.dtype)
 
 
+@pytest.mark.parametrize("dt,causal", [("f16", True), ("f16", False), ("bf16", False)])
+def test_full_size_forward_eight_wavefront_layout(gpu_lib, dt, causal):
+    """1 x 32 x 4096 x 128 without dropout: 512 units of 256 rows, the size
+    at which the forward takes its eight-wavefront layout (64-key steps,
+    three buffers); fp16 inputs and the non-causal case on it, two heads
+    compared element by element."""
+    w = Workload("full8_%s_c%d" % (dt, causal), 1, 32, 4096, 128, dt, causal=causal, seed=41 + causal)
+    heads = [(0, 0), (0, 17)]
+    log("case %s heads %s" % (w.name, heads))
+    q, k, v, _ = workloads.draw(w)
+    o, lse = run_fwd(gpu_lib, w, q, k, v)
+    eo, elx = oracle_fwd(w, q, k, v, heads=heads)
+    for b, h in heads:
+        compare("O", o[b, h], eo[b, h], w.dtype)
+        compare("LSE", lse[b, h], elx[b, h], w.dtype)
+
+
 def test_long_context_65536_sampled_rows(gpu_lib):
     """N=65536: rows are independent in the forward, so a seeded sample of
     rows (the first, tile-boundary rows at stride 4096, the last, random) of
