@@ -344,9 +344,11 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
     auto end_step = [&](auto m_c, int t) {   // m_c: t % NBUF
         constexpr int M = decltype(m_c)::value;
         __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");   // no memory operation crosses this point in the IR either
         // vmcnt(LOADS (NBUF - 2)), lgkmcnt(0)
         __builtin_amdgcn_s_waitcnt(0x0070 | (LOADS * (NBUF - 2)));
         __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         load_kv(t + 1 + NBUF, (M + 1) % NBUF, t + NBUF, M);   // K_{t+1+NBUF}, V_{t+NBUF}
     };
