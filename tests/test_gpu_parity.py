@@ -494,15 +494,17 @@ def test_identity_values_expose_zero_pattern(gpu_lib, d, p):
             assert np.array_equal(got, visible)
 
 
-def test_tile_boundary_probe_at_full_shape(gpu_lib):
+@pytest.mark.parametrize("p,H", [(0.1, 2), (0.0, 32)])
+def test_tile_boundary_probe_at_full_shape(gpu_lib, p, H):
     """Training shape: V has one-hot columns on 128 keys at tile boundaries,
     so O[:, c] = P~[:, probe_c] and its zero pattern must equal the oracle's
     keep & causal pattern exactly; dO one-hot on the probe rows exposes rows
-    of P~ through dV."""
-    w = workloads.WORKLOADS["train_dropout"]
-    B, H, N, d = 1, 2, w.N, w.d
-    w = Workload("probe", B, H, N, d, "bf16", causal=True, dropout_p=w.dropout_p,
-                 backward=True, seed=17, dropout_seed=w.dropout_seed)
+    of P~ through dV.  Without dropout, 32 heads: the forward's
+    eight-wavefront layout (64-key steps)."""
+    w0 = workloads.WORKLOADS["train_dropout"]
+    B, N, d = 1, w0.N, w0.d
+    w = Workload("probe", B, H, N, d, "bf16", causal=True, dropout_p=p,
+                 backward=True, seed=17, dropout_seed=w0.dropout_seed)
     q, k, _, _ = workloads.draw(w)
     probes = []
     for t in np.linspace(1, N // 32 - 1, 43).astype(int) * 32:
@@ -516,12 +518,16 @@ def test_tile_boundary_probe_at_full_shape(gpu_lib):
         do[:, :, j, c] = 1.0
     o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do)
     rows = np.arange(N)
+    o_h, dv_h = o.float().cpu().numpy(), dv.float().cpu().numpy()
     for h in range(H):
-        keep = oracle.dropout_mask(N, p32(w.dropout_p), w.dropout_seed, 0, h).astype(bool)
+        if p > 0:
+            keep = oracle.dropout_mask(N, p32(w.dropout_p), w.dropout_seed, 0, h).astype(bool)
+        else:
+            keep = np.ones((N, N), dtype=bool)
         for c, j in enumerate(probes):
             col_expect = keep[:, j] & (rows >= j)      # P~[:, j] != 0
-            col_got = o[0, h, :, c].float().cpu().numpy() != 0
+            col_got = o_h[0, h, :, c] != 0
             assert np.array_equal(col_got, col_expect), (h, c, j)
             row_expect = keep[j, :] & (rows <= j)      # P~[j, :] != 0
-            row_got = dv[0, h, :, c].float().cpu().numpy() != 0
+            row_got = dv_h[0, h, :, c] != 0
             assert np.array_equal(row_got, row_expect), (h, c, j)
