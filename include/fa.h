@@ -79,7 +79,8 @@ typedef enum fa_dtype {
  *                Philox-4x32-10 block (Salmon et al., SC'11) with counter
  *                (col >> 3, row, h, b) and key (seed low 32, seed high 32);
  *                lane 2w is the low and lane 2w+1 the high half of output
- *                word w; kept iff lane >= round(p * 65536).
+ *                word w; kept iff lane >= round(p * 65536).  A p > 0 that
+ *                rounds to a zero threshold (p < 2^-17) is FA_EUNSUPPORTED.
  *   seed       : dropout seed (ignored when dropout_p == 0).
  *   out_f32    : 0 -> outputs (o, dq, dk, dv) in `dtype`; 1 -> float32.
  *   Nk         : keys (and values) per head for the forward; 0 means N
@@ -90,8 +91,9 @@ typedef enum fa_dtype {
  *                sees every key; a query with no visible key gets O = 0 and
  *                LSE = -inf.  Dropout counters use the query's own row i.
  *                The backward takes the same Nk: dk, dv are [B,H,Nk,d].
- *                One head of q, k or v must stay below 4 GiB (else
- *                FA_EUNSUPPORTED).
+ *                One head of any operand (q, k, v, o, dout or an output)
+ *                must stay below 2 GiB (else FA_EUNSUPPORTED): the kernels
+ *                address a head with signed 32-bit byte offsets.
  */
 typedef struct fa_params {
     int64_t B, H, N, d;
@@ -118,8 +120,9 @@ fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const voi
  * to num_splits contiguous chunks (of a multiple of 64 keys) processed by
  * separate workgroups, for problems with few query rows (decoding, short
  * queries over long keys) that would otherwise leave most of the GPU idle:
- * the sequence-length parallelism of the "FlashAttention-2" section of the
- * interviewsvector.com page, applied to the keys.  Each chunk writes its O,
+ * the parallelism across the sequence dimension of the "FlashAttention-2
+ * Improvements" section of the chipfoundryservices.com page, applied to the
+ * keys.  Each chunk writes its O,
  * normalised over its own keys, and its log-sum-exp to `workspace` (fp32);
  * a second kernel merges them per row with the online-softmax rescaling
  * (LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s).  Same
@@ -185,6 +188,19 @@ fa_status_t fa_bwd_dq(const fa_params_t *p, const void *q, const void *k, const 
  */
 fa_status_t fa_dropout_mask(const fa_params_t *p, int64_t b, int64_t h, uint8_t *mask,
                             void *stream);
+
+/*
+ * Test hook (host only, no HIP call): the order in which the kernels take
+ * their work units.  A kernel's grid has one workgroup per unit, BH heads
+ * times nb blocks per head; workgroup u is dispatched to XCD u % 8, and
+ * unit_of (fa_kernels.hpp) assigns it the head bh[u] and the block rank
+ * rank[u] (rank 0 = the longest block of a causal head), so that each XCD
+ * works through a contiguous range of an order that takes the heads in
+ * groups of `group` and, within a group, blocks rank by rank.  bh and rank
+ * are host arrays of BH * nb entries.  FA_EINVAL for BH, nb or group < 1 or
+ * BH * nb or group * nb >= 2^31.
+ */
+fa_status_t fa_unit_order(int64_t BH, int64_t nb, int32_t group, uint32_t *bh, uint32_t *rank);
 
 /* Static description of a status code. */
 const char *fa_status_str(fa_status_t s);

@@ -78,6 +78,8 @@ def load():
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_unit_order.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, vp, vp]
+    lib.fa_unit_order.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -115,10 +117,21 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _need(t, like, name):
-    if not t.is_cuda or not t.is_contiguous() or t.shape != like.shape:
-        raise ValueError("%s must be a contiguous device tensor of shape %s" %
-                         (name, tuple(like.shape)))
+def _need(t, like, name, dtype=None, shape=None):
+    shape = tuple(like.shape) if shape is None else tuple(shape)
+    if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+        raise ValueError("%s must be a contiguous device tensor of shape %s" % (name, shape))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must have dtype %s (got %s)" % (name, dtype, t.dtype))
+    if t.device != like.device:
+        raise ValueError("%s must be on %s (got %s)" % (name, like.device, t.device))
+
+
+def _check_bwd_inputs(q, o, lse, dout, out_f32):
+    """o in the forward's output type, lse float32 [B,H,N], dout in q's type."""
+    _need(o, q, "o", dtype=torch.float32 if out_f32 else q.dtype)
+    _need(lse, q, "lse", dtype=torch.float32, shape=q.shape[:3])
+    _need(dout, q, "dout", dtype=q.dtype)
 
 
 def _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32):
@@ -181,8 +194,7 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dropout_p=0.0, seed=0,
     (k, v and so dk, dv may hold Nk != N keys)."""
     lib = load()
     p = _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32)
-    for t, n in ((o, "o"), (dout, "dout")):
-        _need(t, q, n)
+    _check_bwd_inputs(q, o, lse, dout, out_f32)
     out_dtype = torch.float32 if out_f32 else q.dtype
     dq = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     dk = torch.empty(k.shape, dtype=out_dtype, device=q.device)
@@ -205,14 +217,15 @@ class Problem:
                  out_f32=False):
         lib = load()
         self.q, self.k, self.v, self.dout = q, k, v, dout
-        self.p = _params_for(q, scale, causal, dropout_p, seed, out_f32)
+        self.p = _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32)
         odt = torch.float32 if out_f32 else q.dtype
         self.o = torch.empty(q.shape, dtype=odt, device=q.device)
         self.lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
         if dout is not None:
+            _need(dout, q, "dout", dtype=q.dtype)
             self.dq = torch.empty(q.shape, dtype=odt, device=q.device)
-            self.dk = torch.empty(q.shape, dtype=odt, device=q.device)
-            self.dv = torch.empty(q.shape, dtype=odt, device=q.device)
+            self.dk = torch.empty(k.shape, dtype=odt, device=q.device)
+            self.dv = torch.empty(k.shape, dtype=odt, device=q.device)
             n = lib.fa_bwd_workspace_bytes(ctypes.byref(self.p))
             self.ws = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
         self._s = _stream(q)
@@ -239,6 +252,17 @@ class Problem:
         self.bwd_prepare()
         self.bwd_dkdv()
         self.bwd_dq()
+
+
+def unit_order(BH, nb, group):
+    """(bh, rank) uint32 arrays of the kernels' work-unit order for BH heads
+    of nb blocks each and heads grouped by ``group`` (host only)."""
+    import numpy as np
+    lib = load()
+    bh = np.empty(BH * nb, dtype=np.uint32)
+    rank = np.empty(BH * nb, dtype=np.uint32)
+    _check(lib.fa_unit_order(BH, nb, group, bh.ctypes.data, rank.ctypes.data))
+    return bh, rank
 
 
 def dropout_mask(B, H, N, dropout_p, seed, b, h, device="cuda"):

@@ -3,6 +3,7 @@
 // so a rejected call never touches the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -10,6 +11,37 @@
 
 #include "../../include/fa.h"
 #include "fa_kernels.hpp"
+
+namespace fa {
+
+// Heads per group of the unit order: enough heads that their blocks fill
+// the resident workgroup slots of one XCD (CUs / 8 times the workgroups per
+// CU) twice, but no more than one XCD's share of the heads (a group spread
+// over two XCDs would give one of them all the long causal blocks).
+// Measured on the training shape (4 x 32 x 4096 x 128) this takes the step
+// from 3.46 ms (one group per XCD's share) or 3.37 ms (slots filled once)
+// to 3.29 ms.  The CU count is read once per device.
+uint32_t unit_group(int64_t BH, int64_t nb, int wg_per_cu) {
+    static std::atomic<int> cu_count[64];
+    int n = 256, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        n = cu_count[dev].load(std::memory_order_relaxed);
+        if (n <= 0) {
+            int c = 0;
+            n = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0
+                    ? c : 256;
+            cu_count[dev].store(n, std::memory_order_relaxed);
+        }
+    }
+    const int64_t per_xcd = n / (int)kXcds > 0 ? n / (int)kXcds : 1;
+    const int64_t slots = per_xcd * (wg_per_cu > 0 ? wg_per_cu : 1);
+    int64_t g = nb > 0 ? (2 * slots + nb - 1) / nb : 1;
+    const int64_t share = BH / (int64_t)kXcds;
+    if (g > share) g = share;
+    return (uint32_t)(g < 1 ? 1 : g);
+}
+
+}  // namespace fa
 
 namespace {
 
@@ -33,6 +65,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t elem_bytes(int32_t dtype) { return dtype == FA_F32 ? 4 : 2; }
 
+uint32_t drop_threshold(float p) { return (uint32_t)std::llround((double)p * 65536.0); }
+float keep_scale(float p) { return (float)(1.0 / (1.0 - (double)p)); }
+
 // Checks shared by every entry point.  *empty is set when there is nothing
 // to compute (a zero extent).
 fa_status_t check_params(const fa_params_t *p, bool *empty) {
@@ -53,13 +88,18 @@ fa_status_t check_params(const fa_params_t *p, bool *empty) {
         return fail(FA_EINVAL, "scale must be finite and positive (got %g)", (double)p->scale);
     if (!(p->dropout_p >= 0.f && p->dropout_p < 1.f))
         return fail(FA_EINVAL, "dropout_p must be in [0, 1) (got %g)", (double)p->dropout_p);
+    // The packed keep-mask compares of the 16-bit kernels represent
+    // thresholds 1 .. 65536 only; T = 0 would keep every element.
+    if (p->dropout_p > 0.f && drop_threshold(p->dropout_p) == 0)
+        return fail(FA_EUNSUPPORTED, "dropout_p=%g rounds to a zero 16-bit threshold (p < 2^-17)",
+                    (double)p->dropout_p);
     if (p->out_f32 != 0 && p->out_f32 != 1) return fail(FA_EINVAL, "out_f32 must be 0 or 1");
     if (p->Nk < 0) return fail(FA_EINVAL, "Nk=%d is negative", (int)p->Nk);
-    // One head of any operand is addressed with 32-bit byte offsets.
+    // One head of any operand is addressed with signed 32-bit byte offsets.
     const double head_bytes = (double)(p->Nk > p->N ? p->Nk : p->N) * (double)p->d *
                               (p->dtype == FA_F32 || p->out_f32 ? 4.0 : 2.0);
-    if (head_bytes >= 4294967296.0)
-        return fail(FA_EUNSUPPORTED, "one head of %.3g bytes exceeds 4 GiB", head_bytes);
+    if (head_bytes >= 2147483648.0)
+        return fail(FA_EUNSUPPORTED, "one head of %.3g bytes reaches 2 GiB", head_bytes);
     // B*H*N*d must be addressable; the product of the extents is bounded
     // piecewise to avoid overflow in the check itself.
     const double total = (double)p->B * (double)p->H * (double)p->N * (double)p->d;
@@ -78,8 +118,6 @@ fa::Elem elem(int32_t dtype) {
     return dtype == FA_F32 ? fa::Elem::F32 : dtype == FA_BF16 ? fa::Elem::BF16 : fa::Elem::F16;
 }
 
-uint32_t drop_threshold(float p) { return (uint32_t)std::llround((double)p * 65536.0); }
-float keep_scale(float p) { return (float)(1.0 / (1.0 - (double)p)); }
 
 // The workspace holds two fp32 arrays of one value per query row, each
 // padded to 256 bytes: D_i / c, then -lse_i log2(e).
@@ -334,6 +372,20 @@ fa_status_t fa_dropout_mask(const fa_params_t *p, int64_t b, int64_t h, uint8_t 
                                               (uint32_t)(p->seed >> 32), b, h, mask,
                                               reinterpret_cast<hipStream_t>(stream)),
                       "fa_dropout_mask launch");
+}
+
+fa_status_t fa_unit_order(int64_t BH, int64_t nb, int32_t group, uint32_t *bh, uint32_t *rank) {
+    if (BH < 1 || nb < 1 || group < 1) return fail(FA_EINVAL, "BH, nb and group must be >= 1");
+    if (BH * nb > 0x7fffffffLL || (int64_t)group * nb > 0x7fffffffLL)
+        return fail(FA_EINVAL, "BH * nb and group * nb must stay below 2^31");
+    if (!bh || !rank) return fail(FA_EINVAL, "output arrays must not be NULL");
+    const uint32_t U = (uint32_t)(BH * nb);
+    for (uint32_t u = 0; u < U; ++u) {
+        const fa::Unit x = fa::unit_of(u, U, (uint32_t)BH, (uint32_t)nb, (uint32_t)group);
+        bh[u] = x.bh;
+        rank[u] = x.rank;
+    }
+    return ok();
 }
 
 const char *fa_status_str(fa_status_t s) {

@@ -94,9 +94,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
     const int lq = lane % 32, g = lane / 32;
 
     const int64_t BH = a.B * a.H;
-    const int64_t u = blockIdx.x;
-    const int64_t bh = u % BH;
-    const int64_t kblk = u / BH;                  // causal: low key blocks (most work) first
+    const int64_t nkb = (a.Nk + BK - 1) / BK;
+    const Unit un = unit_of(blockIdx.x, gridDim.x, (uint32_t)BH, (uint32_t)nkb, a.group);
+    const int64_t bh = un.bh;
+    const int64_t kblk = un.rank;                 // causal: low key blocks (most work) first
     const int64_t N = a.N, Nk = a.Nk;
     const int64_t off = Nk - N;                   // causal: query i sees keys j <= i + off
     const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
@@ -290,9 +291,9 @@ __global__ void __launch_bounds__(256, (DqTile<T, D>::MIN_WG_PER_CU)) bwd_dq_ker
 
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
-    const int64_t u = blockIdx.x;
-    const int64_t bh = u % BH;
-    const int64_t qb = CAUSAL ? (nqb - 1 - u / BH) : (u / BH);
+    const Unit un = unit_of(blockIdx.x, gridDim.x, (uint32_t)BH, (uint32_t)nqb, a.group);
+    const int64_t bh = un.bh;
+    const int64_t qb = CAUSAL ? (nqb - 1 - un.rank) : un.rank;
     const int64_t N = a.N, Nk = a.Nk;
     const int64_t off = Nk - N;                   // causal: query i sees keys j <= i + off
     const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
@@ -419,15 +420,18 @@ static hipError_t launch_pre_t(const BwdArgs &a, hipStream_t stream) {
 template <typename T, int D>
 static hipError_t launch_dkdv_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
     using TL = DkdvTile<T, D>;
-    const int64_t units = a.B * a.H * ((a.Nk + TL::BK - 1) / TL::BK);
+    const int64_t nkb = (a.Nk + TL::BK - 1) / TL::BK;
+    const int64_t units = a.B * a.H * nkb;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
+    BwdArgs b = a;
+    b.group = unit_group(a.B * a.H, nkb, 1);
     if (causal) {
-        if (dropout) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, true, false>), grid, block, 0, stream, b);
     } else {
-        if (dropout) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, false, false>), grid, block, 0, stream, b);
     }
     return hipGetLastError();
 }
@@ -435,15 +439,18 @@ static hipError_t launch_dkdv_t(bool causal, bool dropout, const BwdArgs &a, hip
 template <typename T, int D>
 static hipError_t launch_dq_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
     using TL = DqTile<T, D>;
-    const int64_t units = a.B * a.H * ((a.N + TL::BQ - 1) / TL::BQ);
+    const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
+    const int64_t units = a.B * a.H * nqb;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
+    BwdArgs b = a;
+    b.group = unit_group(a.B * a.H, nqb, TL::MIN_WG_PER_CU);
     if (causal) {
-        if (dropout) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((bwd_dq_kernel<T, D, true, false>), grid, block, 0, stream, b);
     } else {
-        if (dropout) hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((bwd_dq_kernel<T, D, false, false>), grid, block, 0, stream, b);
     }
     return hipGetLastError();
 }

@@ -67,9 +67,9 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
 
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
-    const int64_t u = blockIdx.x;
-    const int64_t bh = u % BH;
-    const int64_t qb = CAUSAL ? (nqb - 1 - u / BH) : (u / BH);
+    const Unit un = unit_of(blockIdx.x, gridDim.x, (uint32_t)BH, (uint32_t)nqb, a.group);
+    const int64_t bh = un.bh;
+    const int64_t qb = CAUSAL ? (nqb - 1 - un.rank) : un.rank;
     const int N = (int)a.N, Nk = (int)a.Nk;
     const int64_t off = (int64_t)Nk - N;   // causal: row i sees keys j <= i + off
     const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
@@ -385,15 +385,18 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
 template <typename T, int D>
 static hipError_t launch_dq16_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
     using TL = Dq16Tile<T, D>;
-    const int64_t units = a.B * a.H * ((a.N + TL::BQ - 1) / TL::BQ);
+    const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
+    const int64_t units = a.B * a.H * nqb;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
+    BwdArgs b = a;
+    b.group = unit_group(a.B * a.H, nqb, 1);
     if (causal) {
-        if (dropout) hipLaunchKernelGGL((dq16_kernel<T, D, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((dq16_kernel<T, D, true, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((dq16_kernel<T, D, true, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((dq16_kernel<T, D, true, false>), grid, block, 0, stream, b);
     } else {
-        if (dropout) hipLaunchKernelGGL((dq16_kernel<T, D, false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((dq16_kernel<T, D, false, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((dq16_kernel<T, D, false, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((dq16_kernel<T, D, false, false>), grid, block, 0, stream, b);
     }
     return hipGetLastError();
 }

@@ -98,9 +98,10 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     const int lq = lane & 31, g = lane >> 5;
 
     const int64_t BH = a.B * a.H;
-    const int64_t u = blockIdx.x;
-    const int64_t bh = u % BH;
-    const int kblk = (int)(u / BH);                       // causal: low key blocks (most work) first
+    const int64_t nkb = (a.Nk + BK - 1) / BK;
+    const Unit un = unit_of(blockIdx.x, gridDim.x, (uint32_t)BH, (uint32_t)nkb, a.group);
+    const int64_t bh = un.bh;
+    const int kblk = (int)un.rank;                        // causal: low key blocks (most work) first
     const int N = (int)a.N, Nk = (int)a.Nk;
     const int off = Nk - N;                  // causal: query i sees keys j <= i + off
     const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
@@ -587,15 +588,18 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 template <typename T, int D>
 static hipError_t launch_dkdv16_t(bool causal, bool dropout, const BwdArgs &a, hipStream_t stream) {
     using TL = Dkdv16Tile<T, D>;
-    const int64_t units = a.B * a.H * ((a.Nk + TL::BK - 1) / TL::BK);
+    const int64_t nkb = (a.Nk + TL::BK - 1) / TL::BK;
+    const int64_t units = a.B * a.H * nkb;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
+    BwdArgs b = a;
+    b.group = unit_group(a.B * a.H, nkb, 1);
     if (causal) {
-        if (dropout) hipLaunchKernelGGL((dkdv16_kernel<T, D, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((dkdv16_kernel<T, D, true, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((dkdv16_kernel<T, D, true, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((dkdv16_kernel<T, D, true, false>), grid, block, 0, stream, b);
     } else {
-        if (dropout) hipLaunchKernelGGL((dkdv16_kernel<T, D, false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((dkdv16_kernel<T, D, false, false>), grid, block, 0, stream, a);
+        if (dropout) hipLaunchKernelGGL((dkdv16_kernel<T, D, false, true>), grid, block, 0, stream, b);
+        else hipLaunchKernelGGL((dkdv16_kernel<T, D, false, false>), grid, block, 0, stream, b);
     }
     return hipGetLastError();
 }

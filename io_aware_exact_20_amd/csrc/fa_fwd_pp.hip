@@ -101,10 +101,10 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
 
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
-    const int64_t u = blockIdx.x;
-    const int64_t bh = u % BH;
-    const int64_t qi = (u / BH) / a.kv_splits;
-    const int split = (int)((u / BH) % a.kv_splits);
+    const Unit un = unit_of(blockIdx.x, gridDim.x, (uint32_t)BH, (uint32_t)(nqb * a.kv_splits), a.group);
+    const int64_t bh = un.bh;
+    const int64_t qi = un.rank / (uint32_t)a.kv_splits;
+    const int split = (int)(un.rank % (uint32_t)a.kv_splits);
     const int64_t qb = CAUSAL ? (nqb - 1 - qi) : qi;
     const int N = (int)a.N, Nk = (int)a.Nk;
     const size_t head = (size_t)bh * (size_t)N * D, head_kv = (size_t)bh * (size_t)Nk * D;
@@ -444,7 +444,9 @@ static hipError_t launch_fwd_pp_k(const FwdArgs &a, hipStream_t stream) {
     const int64_t units = a.B * a.H * nqb * a.kv_splits;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
-    hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL, DROPOUT, W4>), grid, block, 0, stream, a);
+    FwdArgs b = a;
+    b.group = unit_group(a.B * a.H, nqb * a.kv_splits, TL::WG_PER_CU);
+    hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL, DROPOUT, W4>), grid, block, 0, stream, b);
     return hipGetLastError();
 }
 

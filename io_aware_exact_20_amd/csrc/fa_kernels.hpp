@@ -9,6 +9,42 @@ namespace fa {
 
 enum class Elem { F32 = 0, BF16 = 1, F16 = 2 };
 
+// ------------------------------------------------------------ unit order
+//
+// Every kernel's grid is one workgroup per work unit (b, h, block of query
+// rows or keys).  The dispatcher hands workgroup u to XCD u % 8, as that
+// XCD's (u / 8)-th workgroup, and each XCD has its own L2.  unit_of()
+// renumbers u so that each XCD takes a contiguous range of one order over
+// all units: heads in groups of G, and within a group block rank by block
+// rank (rank 0 first: the longest causal block), the group's heads
+// alternating.  The heads live on an XCD at any time are then those of one
+// or two groups -- their K/V (forward) or Q/dO (backward) rows stay in that
+// XCD's L2 -- while the longest units still start first.  The launchers
+// pick G (unit_group) as the number of heads whose blocks fill the XCD's
+// resident workgroup slots twice, capped at one XCD's share of the heads.
+// Any G >= 1 gives a bijection; only locality and load balance depend on it.
+constexpr uint32_t kXcds = 8;
+
+struct Unit {
+    uint32_t bh;      // b * H + h
+    uint32_t rank;    // block rank within the head, 0 .. nb - 1
+};
+
+__host__ __device__ inline Unit unit_of(uint32_t u, uint32_t U, uint32_t BH, uint32_t nb,
+                                        uint32_t G) {
+    const uint32_t per = U / kXcds, extra = U % kXcds;
+    const uint32_t x = u % kXcds, s = u / kXcds;
+    const uint32_t v = x * per + (x < extra ? x : extra) + s;    // position in the order
+    const uint32_t gsz = G * nb;
+    const uint32_t grp = v / gsz, r = v % gsz;
+    const uint32_t heads = BH - grp * G < G ? BH - grp * G : G;  // the last group may be short
+    return Unit{grp * G + r % heads, r / heads};
+}
+
+// Heads per group for BH heads of nb units each and `wg_per_cu` resident
+// workgroups per CU (host side; the CU count is the current device's).
+uint32_t unit_group(int64_t BH, int64_t nb, int wg_per_cu);
+
 struct FwdArgs {
     const void *q, *k, *v;
     void *o;
@@ -24,6 +60,7 @@ struct FwdArgs {
     uint32_t drop_T;      // 16-bit drop threshold round(p * 65536)
     uint32_t seed_lo, seed_hi;
     int32_t out_f32;
+    uint32_t group;       // heads per group of the unit order (unit_of)
 };
 
 struct BwdArgs {
@@ -40,6 +77,7 @@ struct BwdArgs {
     uint32_t drop_T;
     uint32_t seed_lo, seed_hi;
     int32_t out_f32;      // o, dout and the gradients are fp32 when set
+    uint32_t group;       // heads per group of the unit order (unit_of), set by each launcher
 };
 
 // Each launcher enqueues its kernels on `stream` and returns the status of

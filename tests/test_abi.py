@@ -81,12 +81,93 @@ def test_bad_flags_and_key_length(lib):
     p = _p()
     p.Nk = -1
     assert _fwd(lib, p) == fa.FA_EINVAL
-    # one head past 4 GiB (32-bit byte offsets)
-    p = _p(N=2**24, d=128)
+    # one head of 2 GiB or more (signed 32-bit byte offsets in the kernels)
+    p = _p(N=2**23, d=128)
     assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
     p = _p(N=16, d=128)
-    p.Nk = 2**24
+    p.Nk = 2**23
     assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
+    p = _p(N=2**22, d=128, dtype=fa.F32)
+    assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
+    p = _p(N=2**22, d=128, out_f32=True)
+    assert _fwd(lib, p) == fa.FA_EUNSUPPORTED
+    p = _p(N=2**23 - 64, d=128)          # just below: validation passes, pointers are checked next
+    assert _fwd(lib, p, ptr=None) == fa.FA_EINVAL
+    assert "q is NULL" in lib.fa_last_error().decode()
+
+
+def test_dropout_below_one_threshold_step_is_rejected(lib):
+    """keep <=> lane >= round(p * 65536): a p > 0 whose threshold rounds to 0
+    would keep everything, which the packed compares cannot express, so it is
+    refused; p = 2^-17 rounds to T = 1 and is accepted."""
+    for p in (1e-6, 2.0**-17 * 0.99):
+        assert _fwd(lib, _p(dropout_p=p)) == fa.FA_EUNSUPPORTED
+        assert "threshold" in lib.fa_last_error().decode()
+    assert _fwd(lib, _p(dropout_p=2.0**-17), ptr=None) == fa.FA_EINVAL   # past validation
+
+
+def _keep_mask2_emulated(lanes, T):
+    """The packed 16-bit compare of the kernels, emulated: kc = ((T ^ 0x8000) - 1)
+    & 0xFFFF as a signed 16-bit value, d = saturate(kc - (lane ^ 0x8000)) in
+    signed 16-bit arithmetic, kept where d < 0."""
+    import numpy as np
+    kc = np.int32(np.int16(np.uint16(((T ^ 0x8000) - 1) & 0xFFFF)))
+    lane_s = (lanes.astype(np.int32) ^ 0x8000).astype(np.uint16).astype(np.int16).astype(np.int32)
+    d = np.clip(kc - lane_s, -32768, 32767)
+    return d < 0
+
+
+@pytest.mark.parametrize("T", [1, 2, 6554, 32767, 32768, 32769, 65535, 65536])
+def test_packed_keep_compare_matches_threshold(T):
+    """For every accepted threshold the packed compare keeps exactly the lanes
+    with lane >= T, over all 65536 lane values."""
+    import numpy as np
+    lanes = np.arange(65536, dtype=np.int64)
+    assert np.array_equal(_keep_mask2_emulated(lanes, T), lanes >= T)
+
+
+def test_packed_keep_compare_cannot_express_zero_threshold():
+    import numpy as np
+    lanes = np.arange(65536, dtype=np.int64)
+    assert not np.array_equal(_keep_mask2_emulated(lanes, 0), lanes >= 0)
+
+
+@pytest.mark.parametrize("BH,nb,group", [(128, 32, 1), (128, 16, 2), (32, 16, 2), (128, 8, 4),
+                                         (7, 5, 3), (3, 1, 8), (13, 37, 2), (1, 100, 1),
+                                         (5, 3, 64)])
+def test_unit_order_is_a_head_grouped_bijection(BH, nb, group):
+    """Workgroup u runs on XCD u % 8; every XCD takes a contiguous range of
+    the head-grouped, rank-major order, so each unit is taken exactly once,
+    ranks of one head come in increasing order, and an XCD holds at most
+    ceil(range / nb) + 1 distinct heads' worth of groups at a time."""
+    import numpy as np
+    bh, rank = fa.unit_order(BH, nb, group)
+    U = BH * nb
+    assert sorted(zip(bh.tolist(), rank.tolist())) == [(h, r) for h in range(BH) for r in range(nb)]
+    # the order v = position within the XCD-major listing
+    per, extra = divmod(U, 8)
+    order = []
+    for x in range(8):
+        order += [u for u in range(x, U, 8)]
+    seq = [(int(bh[u]), int(rank[u])) for u in order]
+    # group-major, then rank, then head within the group
+    key = [(h // group, r, h) for h, r in seq]
+    assert key == sorted(key)
+    # the units of one XCD cover few groups: at most two partial groups plus whole ones
+    for x in range(8):
+        units = [u for u in range(x, U, 8)]
+        groups = {int(bh[u]) // group for u in units}
+        assert len(groups) <= len(units) // (group * nb) + 2
+
+
+def test_unit_order_rejects_bad_arguments(lib):
+    import numpy as np
+    out = np.empty(4, dtype=np.uint32)
+    ptr = out.ctypes.data
+    assert lib.fa_unit_order(0, 4, 1, ptr, ptr) == fa.FA_EINVAL
+    assert lib.fa_unit_order(1, 4, 0, ptr, ptr) == fa.FA_EINVAL
+    assert lib.fa_unit_order(1, 4, 1, None, ptr) == fa.FA_EINVAL
+    assert lib.fa_unit_order(2**20, 2**12, 1, ptr, ptr) == fa.FA_EINVAL
 
 
 def test_backward_workspace_follows_the_query_rows(lib):
