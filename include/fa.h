@@ -181,6 +181,24 @@ fa_status_t fa_bwd_dq(const fa_params_t *p, const void *q, const void *k, const 
                       size_t workspace_bytes, void *stream);
 
 /*
+ * The backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results as fa_bwd, but the row statistics
+ * live in a static device array of fa_bwd_noalloc_max_workspace_bytes()
+ * bytes (32 MiB: B*H*N <= 4,194,304 query rows), one copy per device, held
+ * until the process ends.  The array's device address is looked up on the
+ * first call on each device (with that device current); no call allocates
+ * or frees memory.  A larger problem is refused with FA_EINVAL (use fa_bwd
+ * with a workspace).  Every call on a device shares that device's array,
+ * so calls that overlap on one device (other streams, other threads) race;
+ * nothing in it needs clearing between calls.
+ */
+size_t fa_bwd_noalloc_max_workspace_bytes(void);
+fa_status_t fa_bwd_noalloc(const fa_params_t *p, const void *q, const void *k, const void *v,
+                           const void *o, const float *lse, const void *dout,
+                           void *dq, void *dk, void *dv, void *stream);
+
+/*
  * Test hook: writes the dropout keep mask of plane (b, h) -- mask[row*N +
  * col] = 1 when kept, 0 when dropped -- using the same device generator as
  * the attention kernels.  Only B, H, N, dropout_p and seed of p are read

@@ -78,6 +78,10 @@ def load():
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fa_bwd_noalloc.restype = ctypes.c_int
+    lib.fa_bwd_noalloc_max_workspace_bytes.argtypes = []
+    lib.fa_bwd_noalloc_max_workspace_bytes.restype = sz
     lib.fa_unit_order.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, vp, vp]
     lib.fa_unit_order.restype = ctypes.c_int
     _lib = lib
@@ -205,6 +209,28 @@ def bwd(q, k, v, o, lse, dout, scale=None, causal=False, dropout_p=0.0, seed=0,
     _check(lib.fa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                       _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                       workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, scale=None, causal=False, dropout_p=0.0, seed=0,
+                out_f32=False, out=None):
+    """``fa_bwd_noalloc``: the backward with the library's static scratch in
+    place of a workspace.  ``out`` = (dq, dk, dv) preallocated by the caller
+    (allocated here when None)."""
+    lib = load()
+    p = _fwd_params(q, k, v, scale, causal, dropout_p, seed, out_f32)
+    _check_bwd_inputs(q, o, lse, dout, out_f32)
+    out_dtype = torch.float32 if out_f32 else q.dtype
+    if out is None:
+        out = (torch.empty(q.shape, dtype=out_dtype, device=q.device),
+               torch.empty(k.shape, dtype=out_dtype, device=q.device),
+               torch.empty(k.shape, dtype=out_dtype, device=q.device))
+    dq, dk, dv = out
+    _need(dq, q, "dq", dtype=out_dtype)
+    _need(dk, k, "dk", dtype=out_dtype)
+    _need(dv, k, "dv", dtype=out_dtype)
+    _check(lib.fa_bwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _stream(q)))
     return dq, dk, dv
 
 

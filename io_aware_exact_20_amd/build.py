@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_bwd.hip", "fa_bwd16.hip", "fa_dkdv16.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_bwd.hip", "fa_bwd16.hip", "fa_dkdv16.hip",
+           "fa_noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

@@ -61,6 +61,16 @@ fa_status_t ok() {
     return FA_OK;
 }
 
+}  // namespace
+
+namespace fa {
+
+fa_status_t record_error(fa_status_t s, const char *msg) { return fail(s, "%s", msg); }
+
+}  // namespace fa
+
+namespace {
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 size_t elem_bytes(int32_t dtype) { return dtype == FA_F32 ? 4 : 2; }

@@ -160,6 +160,25 @@ def test_unit_order_is_a_head_grouped_bijection(BH, nb, group):
         assert len(groups) <= len(units) // (group * nb) + 2
 
 
+def test_noalloc_backward_validates_before_any_device_call(lib):
+    """fa_bwd_noalloc refuses bad parameters, bad pointers and problems beyond
+    its static scratch (B*H*N > 4,194,304 rows) without a HIP call; empty
+    problems return FA_OK."""
+    assert lib.fa_bwd_noalloc_max_workspace_bytes() == 32 << 20
+    args = [FAKE] * 9
+    assert lib.fa_bwd_noalloc(ctypes.byref(_p(d=80)), *args, None) == fa.FA_EUNSUPPORTED
+    assert lib.fa_bwd_noalloc(ctypes.byref(_p(N=0)), *([None] * 9), None) == fa.FA_OK
+    bad = list(args)
+    bad[4] = MISALIGNED
+    assert lib.fa_bwd_noalloc(ctypes.byref(_p()), *bad, None) == fa.FA_EINVAL
+    assert "lse" in lib.fa_last_error().decode()
+    p = _p(B=1, H=1, N=4194305, d=64)
+    assert lib.fa_bwd_noalloc(ctypes.byref(p), *args, None) == fa.FA_EINVAL
+    assert "static scratch" in lib.fa_last_error().decode()
+    p = _p(B=2, H=4, N=524289, d=64)
+    assert lib.fa_bwd_noalloc(ctypes.byref(p), *args, None) == fa.FA_EINVAL
+
+
 def test_unit_order_rejects_bad_arguments(lib):
     import numpy as np
     out = np.empty(4, dtype=np.uint32)
