@@ -59,8 +59,9 @@ def make_problem(fa, w, dev, with_bwd=True):
                       dropout_p=w.dropout_p, seed=w.dropout_seed)
 
 
-def time_steps(prob, steps, warmup, with_bwd=True):
-    """Wall time per step plus per-stage HIP-event times (ms, per launch)."""
+def time_steps(prob, steps, warmup, with_bwd=True, per_step=False):
+    """Wall time per step plus per-stage HIP-event times (ms, per launch);
+    with per_step, also each step's event time (ms) in a list."""
     stages = [("fwd", prob.fwd)]
     if with_bwd:
         stages += [("bwd_prepare", prob.bwd_prepare), ("bwd_dkdv", prob.bwd_dkdv),
@@ -82,6 +83,8 @@ def time_steps(prob, steps, warmup, with_bwd=True):
     per = {}
     for i, (name, _) in enumerate(stages):
         per[name] = sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps
+    if per_step:
+        return wall, per, [ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]
     return wall, per
 
 
@@ -126,29 +129,140 @@ def traffic_for(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle (forward + backward of whole heads of the same
-    workload) on the host cores for about `budget_s` seconds."""
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _err(got, exact):
+    """(max-abs, mean-abs) of a GPU tensor against a float64 array."""
     import numpy as np
+    e = np.abs(got.detach().double().cpu().numpy() - exact)
+    return float(e.max()), float(e.mean())
+
+
+def oracle_heads(w, q, k, v, do, budget_s, outputs=None, max_heads=None):
+    """The fp64 oracle over whole heads of workload w (forward, or forward +
+    backward when do is given), head after head until budget_s seconds have
+    been spent (at least one head).  Returns (heads done, seconds, errors):
+    with `outputs` (the GPU's o, lse[, dq, dk, dv] of the same inputs), the
+    max/mean-abs error of each on the heads done."""
+    import numpy as np
+    import oracle
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if max_heads:
+        heads = heads[:max_heads]
+    p = float(np.float32(w.dropout_p))
+    done, t_total = [], 0.0
+    errs = {}
+    names = ("O", "LSE", "dQ", "dK", "dV")
+    while len(done) < len(heads) and (not done or t_total < budget_s):
+        b, h = heads[len(done)]
+        args = [x[b, h] for x in (q, k, v)]
+        if do is not None:
+            args = [oracle._f64(a) for a in args] + [oracle._f64(do[b, h])]
+            t0 = time.perf_counter()
+            dq, dk, dv, o, lse = oracle.bwd_one_head(*args, b, h, w.softmax_scale, w.causal, p,
+                                                     w.dropout_seed)
+            t_total += time.perf_counter() - t0
+            exact = (o, lse, dq, dk, dv)
+        else:
+            t0 = time.perf_counter()
+            o, lse = oracle.fwd_rows(q, k, v, b, h, range(w.N), w.softmax_scale, w.causal, p,
+                                     w.dropout_seed)
+            t_total += time.perf_counter() - t0
+            exact = (o, lse)
+        done.append((b, h))
+        if outputs is not None:
+            for nm, got, ex in zip(names, outputs, exact):
+                mx, mn = _err(got[b, h], ex)
+                cur = errs.setdefault(nm, [0.0, 0.0])
+                cur[0] = max(cur[0], mx)
+                cur[1] += mn
+    for nm in errs:
+        errs[nm] = {"max_abs": float("%.3e" % errs[nm][0]),
+                    "mean_abs": float("%.3e" % (errs[nm][1] / len(done)))}
+    return done, t_total, errs
+
+
+def cpu_baseline(w, budget_s: float, outputs=None):
+    """The fp64 oracle (forward + backward of whole heads of the same
+    workload, each with its own (b, h) dropout counters) on the host cores
+    for about `budget_s` seconds."""
     import oracle
     q, k, v, do = workloads.draw(w)
     f_head = w.flops_fwd() / (w.B * w.H) * 3.5
-    done, t_total = 0, 0.0
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    p = float(np.float32(w.dropout_p))
-    while done < len(heads) and t_total < budget_s:
-        b, h = heads[done]
-        t0 = time.perf_counter()
-        oracle.bwd(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                   do[b:b + 1, h:h + 1], w.softmax_scale, w.causal, p, w.dropout_seed)
-        t_total += time.perf_counter() - t0
-        done += 1
-    # Note: the sliced heads are evaluated with (b, h) = (0, 0) dropout keys;
-    # the arithmetic per head is the same.
-    return {"value": f_head * done / t_total / 1e12, "unit": "TFLOP/s",
+    done, t_total, errs = oracle_heads(w, q, k, v, do, budget_s, outputs)
+    n = len(done)
+    return {"value": f_head * n / t_total / 1e12, "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of %d heads (fwd+bwd, N=%d, d=%d, fp64), %.1f s" %
-                      (done, len(heads), w.N, w.d, t_total)}
+            "cpu_model": host_cpu_model(),
+            "sample": "%d of %d heads (fwd+bwd, N=%d, d=%d, fp64), %.1f s; whole workload "
+                      "extrapolated: %.1f s" % (n, w.B * w.H, w.N, w.d, t_total,
+                                                t_total * w.B * w.H / n),
+            "errors_on_sample": errs}
+
+
+def config_table(fa, dev, budget_s=2.0):
+    """Per target workload: GPU time and TFLOP/s (mean of HIP-event timed
+    calls), % of the bf16 peak, the fp64 oracle's CPU time on sampled heads
+    (extrapolated to the whole workload when sampled) and the GPU's
+    max/mean-abs error per output against it on those heads."""
+    import numpy as np
+    import oracle
+    rows = {}
+    names = ["single_head_f32", "small_fwd_bf16", "small_fwd_bf16_causal", "mid_fwdbwd_causal",
+             "long_causal_4k", "long_causal_16k", "long_causal_64k"]
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        q, k, v, do = workloads.draw(w)
+        prob = fa.Problem(q.to(dev), k.to(dev), v.to(dev),
+                          do.to(dev) if do is not None else None, scale=w.softmax_scale,
+                          causal=w.causal, dropout_p=w.dropout_p, seed=w.dropout_seed)
+        reps = 3 if w.N >= 65536 else 10
+        wall, per = time_steps(prob, reps, 2, with_bwd=w.backward)
+        gpu_ms = sum(per.values())
+        F = w.flops_fwd() * (3.5 if w.backward else 1.0)
+        row = {"shape": "%dx%dx%dx%d" % (w.B, w.H, w.N, w.d), "dtype": w.dtype,
+               "causal": w.causal, "pass": "fwd+bwd" if w.backward else "fwd",
+               "gpu_ms": round(gpu_ms, 4), "tflops": round(F / (gpu_ms * 1e-3) / 1e12, 2),
+               "pct_peak": round(100 * F / (gpu_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+        outs = (prob.o, prob.lse) + ((prob.dq, prob.dk, prob.dv) if w.backward else ())
+        if w.N >= 65536:
+            # one head is 1.1 TFLOP of fp64: time an evenly spaced sample of
+            # its rows (a row's cost is proportional to its visible keys) and
+            # scale by the flops of all rows of all heads
+            rws = list(range(0, w.N, 64))
+            t0 = time.perf_counter()
+            eo, el = oracle.fwd_rows(q, k, v, 0, 0, rws, w.softmax_scale, w.causal)
+            t = time.perf_counter() - t0
+            keys = np.array([(r + 1) if w.causal else w.N for r in rws], dtype=np.float64)
+            frac = keys.sum() / (w.N * (w.N + 1) / 2 if w.causal else w.N * w.N)
+            row["oracle"] = {"seconds": round(t, 2), "cores": oracle.num_threads(),
+                             "sample": "%d rows of head (0,0)" % len(rws),
+                             "whole_workload_s_extrapolated": round(t / frac * w.B * w.H, 1)}
+            row["errors_on_sample"] = {nm: dict(zip(("max_abs", "mean_abs"),
+                                                    [float("%.3e" % x) for x in _err(g[0, 0, rws], e)]))
+                                       for nm, g, e in (("O", prob.o, eo), ("LSE", prob.lse, el))}
+        else:
+            done, t, errs = oracle_heads(w, q, k, v, do if w.backward else None, budget_s,
+                                         outputs=outs)
+            n, tot = len(done), w.B * w.H
+            row["oracle"] = {"seconds": round(t, 3), "cores": oracle.num_threads(),
+                             "sample": "%d of %d heads" % (n, tot),
+                             ("whole_workload_s" if n == tot else "whole_workload_s_extrapolated"):
+                                 round(t * tot / n, 2)}
+            row["errors_on_sample"] = errs
+        rows[name] = row
+        log("config %s %s" % (name, row))
+        del prob
+        torch.cuda.empty_cache()
+    return rows
 
 
 def main():
@@ -196,8 +310,10 @@ def main():
     F = w.flops_fwd()
     log("workload %s: B=%d H=%d N=%d d=%d causal p=%g" % (w.name, w.B, w.H, w.N, w.d, w.dropout_p))
     prob = make_problem(fa, w, dev)
-    wall, per = time_steps(prob, args.steps, args.warmup)
+    wall, per, steps_ms = time_steps(prob, args.steps, args.warmup, per_step=True)
     value = 3.5 * F / (wall * 1e-3) / 1e12
+    steps_sorted = sorted(steps_ms)
+    median_ms = (steps_sorted[(len(steps_sorted) - 1) // 2] + steps_sorted[len(steps_sorted) // 2]) / 2
     log("step %.3f ms  -> %.1f TFLOP/s; stages %s" % (wall, value, per))
 
     # Algorithmic flops credited to each kernel: the forward's two products;
@@ -212,15 +328,24 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_for(dominant),
+                "traffic_source": "profiles/traffic.json: rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                                  "per launch, copy-calibrated, taken on the kernel source "
+                                  "whose hash it records (null when the source has changed)",
                 "avg_launch_ms": round(per[dominant], 4)}
 
     extras = {
+        "step_ms": {"mean_wall": round(wall, 4), "median_event": round(median_ms, 4),
+                    "min_event": round(steps_sorted[0], 4), "max_event": round(steps_sorted[-1], 4)},
+        "value_at_median_tflops": round(3.5 * F / (median_ms * 1e-3) / 1e12, 2),
+        "value_at_min_tflops": round(3.5 * F / (steps_sorted[0] * 1e-3) / 1e12, 2),
         "fwd_tflops": round(F / (per["fwd"] * 1e-3) / 1e12, 2),
         "bwd_tflops": round(2.5 * F / (bwd_ms * 1e-3) / 1e12, 2),
         "stage_ms": {k: round(v, 4) for k, v in per.items()},
     }
     extras["fwd_pct_peak"] = round(100 * extras["fwd_tflops"] / PEAK_BF16_TFLOPS, 2)
     extras["bwd_pct_peak"] = round(100 * extras["bwd_tflops"] / PEAK_BF16_TFLOPS, 2)
+    # the headline's outputs (last timed step) for the oracle comparison below
+    head_outputs = tuple(t.cpu() for t in (prob.o, prob.lse, prob.dq, prob.dk, prob.dv))
     del prob
     torch.cuda.empty_cache()
 
@@ -294,9 +419,12 @@ def main():
         extras["decode"] = decode_line(fa, dev)
         log("extras %s" % extras)
 
-    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    cpu = cpu_baseline(w, args.cpu_seconds, head_outputs) if args.cpu_seconds > 0 else None
     if cpu:
         log("cpu baseline %s" % cpu)
+    if not args.no_extras and args.cpu_seconds > 0:
+        # every other target workload: GPU throughput, oracle CPU time and error
+        extras["configs"] = config_table(fa, dev, budget_s=2.0)
 
     out = {
         "metric": METRIC,

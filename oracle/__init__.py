@@ -238,6 +238,21 @@ def bwd(q, k, v, dout, scale: float, causal: bool = False, dropout_p: float = 0.
     return dq, dk, dv, o, lse
 
 
+def bwd_one_head(q, k, v, dout, b: int, h: int, scale: float, causal: bool = False,
+                 dropout_p: float = 0.0, seed: int = 0):
+    """(dq, dk, dv, o, lse) in float64 of one head given as [N, d] arrays,
+    with the dropout counters of head (b, h)."""
+    lib = _load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    N, d = q.shape
+    dq, dk, dv, o = (np.zeros((N, d)) for _ in range(4))
+    lse = np.zeros(N)
+    _check(lib.oracle_bwd_head(N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), float(scale),
+                               int(bool(causal)), float(dropout_p), seed & (2**64 - 1), b, h,
+                               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(o), _ptr(lse)), "bwd")
+    return dq, dk, dv, o, lse
+
+
 def _bwd_cross(lib, q, k, v, dout, scale, causal, dropout_p, seed, heads):
     """bwd for Nq != Nk (k, v [B,H,Nk,d]): dq, o [B,H,Nq,d]; dk, dv [B,H,Nk,d]."""
     B, H, Nq, d = q.shape
