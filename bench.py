@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6        # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_FP8_TFLOPS = 5033.2         # 256 CU x 8192 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, causal, d=128) + % of MFMA peak"
 # Sources of the 16-bit kernels each stage runs (the counters in
@@ -114,6 +115,36 @@ def decode_line(fa, dev, B=1, H=32, N=16, Nk=65536, d=128, splits=16):
         ms = e0.elapsed_time(e1) / 10
         out[name + "_ms"] = round(ms, 4)
         out[name + "_kv_GBs"] = round(kv_bytes / (ms * 1e-3) / 1e9, 1)
+    return out
+
+
+def fp8_lines(fa, dev):
+    """The FP8 (e4m3) forward on the long causal shape (1 x 32 x N x 128,
+    N = 4096 and 16384) and on the training shape without dropout
+    (4 x 32 x 4096 x 128, causal): HIP-event time and TFLOP/s against the
+    bf16 and the fp8 dense peaks."""
+    out = {}
+    for name, (B, H, N) in (("long_causal_4k", (1, 32, 4096)), ("long_causal_16k", (1, 32, 16384)),
+                            ("train_shape", (4, 32, 4096))):
+        w = workloads.Workload("fp8_" + name, B, H, N, 128, "bf16", causal=True, seed=4)
+        args = [t.to(dev) for t in workloads.draw_fp8(w)]
+        for _ in range(3):
+            fa.fwd_fp8(*args, scale=w.softmax_scale, causal=True)
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fa.fwd_fp8(*args, scale=w.softmax_scale, causal=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = w.flops_fwd() / (ms * 1e-3) / 1e12
+        out[name] = {"shape": "%dx%dx%dx128" % (B, H, N), "fwd_ms": round(ms, 4),
+                     "fwd_tflops": round(tf, 2), "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                     "pct_fp8_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2)}
+        del args
+        torch.cuda.empty_cache()
     return out
 
 
@@ -417,6 +448,7 @@ def main():
             torch.cuda.empty_cache()
         extras["head_dims"] = hd
         extras["decode"] = decode_line(fa, dev)
+        extras["fp8_fwd"] = fp8_lines(fa, dev)
         log("extras %s" % extras)
 
     cpu = cpu_baseline(w, args.cpu_seconds, head_outputs) if args.cpu_seconds > 0 else None

@@ -55,7 +55,8 @@ typedef enum fa_status {
 typedef enum fa_dtype {
     FA_F32 = 0,           /* float32 inputs, fp32 matrix-core products */
     FA_BF16 = 1,          /* bfloat16 inputs, fp32 accumulation */
-    FA_F16 = 2            /* float16 inputs, fp32 accumulation */
+    FA_F16 = 2,           /* float16 inputs, fp32 accumulation */
+    FA_FP8_E4M3 = 3       /* OCP e4m3 inputs with per-head descale factors (fa_fwd_fp8 only) */
 } fa_dtype_t;
 
 /*
@@ -114,6 +115,27 @@ typedef struct fa_params {
  */
 fa_status_t fa_fwd(const fa_params_t *p, const void *q, const void *k, const void *v,
                    void *o, float *lse, void *stream);
+
+/*
+ * Forward with FP8 inputs (the FP8 precision of the "FlashAttention-3
+ * (2024)" section of the chipfoundryservices.com page).  q, k, v are
+ * [B,H,N,d] / [B,H,Nk,d] OCP e4m3 bytes (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; no infinities) with p->dtype = FA_FP8_E4M3; the
+ * attention inputs are q * descale_q[b*H + h] (and k, v likewise):
+ * descale_q, descale_k, descale_v are device arrays of B*H positive finite
+ * float32 factors.  Writes o [B,H,N,d] (bfloat16, or float32 with out_f32)
+ * and lse [B,H,N] float32 as fa_fwd does for the dequantized inputs.  Both
+ * products run on the FP8 matrix cores with fp32 accumulation; the
+ * probabilities enter the second product rounded to e4m3 (after scaling by
+ * 2^6), while the row sums and lse use them unrounded, so
+ *     |o - o_exact| <= (2^-4 + n 2^-16) max_j |v_j| (+ output rounding)
+ * per element, n the number of keys the row sees.  d = 128 only and
+ * dropout_p = 0 only (else FA_EUNSUPPORTED); causal, Nk and out_f32 as in
+ * fa_fwd.
+ */
+fa_status_t fa_fwd_fp8(const fa_params_t *p, const void *q, const void *k, const void *v,
+                       const float *descale_q, const float *descale_k, const float *descale_v,
+                       void *o, float *lse, void *stream);
 
 /*
  * Forward with the keys of every (b, h, block of query rows) split into up

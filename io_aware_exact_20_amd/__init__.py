@@ -20,7 +20,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa.so")
 
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
-F32, BF16, F16 = 0, 1, 2
+F32, BF16, F16, FP8_E4M3 = 0, 1, 2, 3
 _DTYPE_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
@@ -58,6 +58,8 @@ def load():
     vp, P, sz = ctypes.c_void_p, ctypes.POINTER(Params), ctypes.c_size_t
     lib.fa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, vp]
@@ -162,6 +164,33 @@ def fwd(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0, out_f32=False)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _check(lib.fa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                       _stream(q)))
+    return o, lse
+
+
+def fwd_fp8(q, k, v, descale_q, descale_k, descale_v, scale=None, causal=False,
+            out_f32=False):
+    """Forward with OCP e4m3 inputs (``fa_fwd_fp8``): q [B,H,N,128], k, v
+    [B,H,Nk,128] as torch.float8_e4m3fn device tensors, descale_* float32
+    [B,H] device tensors (the inputs are q * descale_q[b, h], ...).  Returns
+    (o bfloat16 or float32 [B,H,N,128], lse float32 [B,H,N])."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.float8_e4m3fn:
+            raise ValueError("%s must be torch.float8_e4m3fn (got %s)" % (n, t.dtype))
+    _need(q, q, "q")
+    _need(k, k, "k")
+    _need(v, k, "v")
+    if k.dim() != 4 or k.shape[:2] != q.shape[:2] or k.shape[3] != q.shape[3]:
+        raise ValueError("k, v must be [B, H, Nk, d] with q's B, H, d")
+    B, H, N, d = q.shape
+    for t, n in ((descale_q, "descale_q"), (descale_k, "descale_k"), (descale_v, "descale_v")):
+        _need(t, q, n, dtype=torch.float32, shape=(B, H))
+    p = make_params(B, H, N, d, FP8_E4M3, scale, causal, 0.0, 0, out_f32,
+                    k.shape[2] if k.shape[2] != N else 0)
+    o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(lib.fa_fwd_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(descale_q),
+                          _ptr(descale_k), _ptr(descale_v), _ptr(o), _ptr(lse), _stream(q)))
     return o, lse
 
 

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_bwd.hip", "fa_bwd16.hip", "fa_dkdv16.hip",
-           "fa_noalloc.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_bwd16.hip",
+           "fa_dkdv16.hip", "fa_noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -32,7 +32,8 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 # the dK/dV kernel keeps them in AGPRs (its accumulators need the room).
 KERNEL_FLAGS = ["-fno-honor-nans"]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-PER_SOURCE = {"fa_fwd.hip": KERNEL_FLAGS + VGPR_FORM, "fa_fwd_pp.hip": KERNEL_FLAGS, "fa_bwd16.hip": KERNEL_FLAGS + VGPR_FORM,
+PER_SOURCE = {"fa_fwd.hip": KERNEL_FLAGS + VGPR_FORM, "fa_fwd_pp.hip": KERNEL_FLAGS,
+              "fa_fwd_fp8.hip": KERNEL_FLAGS, "fa_bwd16.hip": KERNEL_FLAGS + VGPR_FORM,
               "fa_dkdv16.hip": KERNEL_FLAGS + VGPR_FORM}
 
 

@@ -216,6 +216,39 @@ size_t fa_fwd_splitkv_workspace_bytes(const fa_params_t *p, int32_t num_splits) 
     return split_workspace_bytes(p, num_splits);
 }
 
+fa_status_t fa_fwd_fp8(const fa_params_t *p, const void *q, const void *k, const void *v,
+                       const float *descale_q, const float *descale_k, const float *descale_v,
+                       void *o, float *lse, void *stream) {
+    if (!p) return fail(FA_EINVAL, "params is NULL");
+    if (p->dtype != FA_FP8_E4M3)
+        return fail(FA_EINVAL, "fa_fwd_fp8 takes dtype FA_FP8_E4M3 (got %d)", (int)p->dtype);
+    // The shared checks, with the output type (bf16 or fp32) standing for
+    // the element size of the largest head.
+    fa_params_t c = *p;
+    c.dtype = FA_BF16;
+    bool empty = false;
+    fa_status_t s = check_params(&c, &empty);
+    if (s != FA_OK) return s;
+    if (p->d != 128) return fail(FA_EUNSUPPORTED, "FP8 inputs need d = 128 (got %lld)", (long long)p->d);
+    if (p->dropout_p != 0.f) return fail(FA_EUNSUPPORTED, "FP8 inputs take no dropout");
+    if (empty) return ok();
+    if ((s = check_ptr(q, "q")) || (s = check_ptr(k, "k")) || (s = check_ptr(v, "v")) ||
+        (s = check_ptr(o, "o")) || (s = check_ptr(lse, "lse")))
+        return s;
+    const float *ds[3] = {descale_q, descale_k, descale_v};
+    const char *dn[3] = {"descale_q", "descale_k", "descale_v"};
+    for (int i = 0; i < 3; ++i)
+        if (!ds[i] || (reinterpret_cast<uintptr_t>(ds[i]) & 3u))
+            return fail(FA_EINVAL, "%s is NULL or not 4-byte aligned", dn[i]);
+    fa::FwdArgs a = fwd_args(&c, q, k, v, o, lse);
+    a.descale_q = descale_q;
+    a.descale_k = descale_k;
+    a.descale_v = descale_v;
+    return hip_status(fa::launch_fwd_fp8((int)p->d, p->causal != 0, a,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                      "fa_fwd_fp8 launch");
+}
+
 fa_status_t fa_fwd_splitkv(const fa_params_t *p, const void *q, const void *k, const void *v,
                            void *o, float *lse, int32_t num_splits, void *workspace,
                            size_t workspace_size, void *stream) {

@@ -61,6 +61,8 @@ struct FwdArgs {
     uint32_t seed_lo, seed_hi;
     int32_t out_f32;
     uint32_t group;       // heads per group of the unit order (unit_of)
+    // FP8 inputs only: fp32 descale factor per (b, h) of Q, K and V ([B*H] each)
+    const float *descale_q, *descale_k, *descale_v;
 };
 
 struct BwdArgs {
@@ -97,6 +99,8 @@ hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const Bwd
 // 16-bit inputs at d = 128: eight wavefronts per workgroup, two per SIMD.
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                          hipStream_t stream);
+// e4m3 inputs at d = 128 with per-(b, h) descale factors; bf16 (or fp32) O.
+hipError_t launch_fwd_fp8(int d, bool causal, const FwdArgs &a, hipStream_t stream);
 // Combines the kv_splits partial results of a split forward into o and lse.
 hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream);
 hipError_t launch_dropout_mask(int64_t N, uint32_t T, uint32_t seed_lo, uint32_t seed_hi,

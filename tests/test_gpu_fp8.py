@@ -1,0 +1,159 @@
+"""GPU parity of the FP8 (e4m3) forward against the fp64 oracle evaluated on
+the dequantized inputs (q8 * descale_q, ...).
+
+Tolerance (derived from the e4m3 format, not stated by the pages): the
+kernel's only approximation beyond fp32 arithmetic is the rounding of the
+probabilities (times 2^6) to e4m3 before the P V product; the row sums and
+LSE use them unrounded.  With w_j the exact weights of row i and e_j the
+relative rounding errors (|e_j| <= 2^-4 for normals; absolute 2^-16 in
+weight units below the smallest normal), O_i - O_exact_i = sum_j w_j e_j v_j,
+so per element
+    |O_ic - O_exact_ic| <= (2^-4 + n_i 2^-16) max_{j visible} |v_jc|
+plus the output's own rounding (half a bf16 ulp) and fp32 slack.  The mean
+over elements is far smaller, since the e_j have random signs: with the e_j
+independent and of rms at most 2^-4/sqrt(3) (uniform within +-2^-4),
+E|O_ic - O_exact_ic| ~ sqrt(2/pi) 2^-4/sqrt(3) sqrt(sum_j w_j^2 v_jc^2), and
+sum_j w_ij^2 v_jc^2 = exp(LSE2_i - 2 LSE_i) O2_ic is exact from the oracle
+run with twice the scale on the values v^2 (LSE2, O2).  The test holds the
+mean error to 1.25 times the mean of that expectation plus half an output
+ulp.  LSE involves no rounding to e4m3: it is held to 1e-4 + n 2^-24 (fp32
+summation of n terms; the fp32 accumulation of the FP8 products leaves
+score errors of a few 1e-5 at these magnitudes, measured)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def visible_vmax(v, N, causal):
+    """max_{j visible to row i} |v_jc| for every (b, h, i, c) and the number
+    of visible keys n_i (causal: j <= i + Nk - N)."""
+    av = np.abs(v)
+    Nk = v.shape[2]
+    if not causal:
+        return np.broadcast_to(av.max(axis=2, keepdims=True), av.shape[:2] + (N, av.shape[3])), \
+            np.full(N, Nk)
+    cm = np.maximum.accumulate(av, axis=2)
+    idx = np.arange(N) + (Nk - N)
+    vis = np.clip(idx, -1, Nk - 1)
+    out = np.where((idx >= 0)[None, None, :, None], cm[:, :, np.maximum(vis, 0), :], 0.0)
+    return out, np.clip(idx + 1, 0, Nk)
+
+
+def expected_abs_error(qd, kd, vd, scale, causal, el):
+    """sqrt(2/pi) 2^-4/sqrt(3) sqrt(sum_j w_ij^2 v_jc^2) per element (see the
+    module docstring), from the oracle with doubled scale on v^2."""
+    eo2, el2 = oracle.fwd(qd, kd, vd * vd, 2.0 * scale, causal)
+    with np.errstate(invalid="ignore", over="ignore"):
+        sw2 = np.where(np.isfinite(el), np.exp(el2 - 2.0 * el), 0.0)
+    return np.sqrt(2.0 / np.pi) * 2.0 ** -4 / np.sqrt(3.0) * np.sqrt(sw2[..., None] * np.nan_to_num(eo2))
+
+
+def check(name, o, lse, eo, else_, vmax, n, out_f32, expect):
+    g = o.detach().double().cpu().numpy()
+    gl = lse.detach().double().cpu().numpy()
+    live = np.isfinite(else_)
+    assert np.array_equal(np.isfinite(gl), live), "rows with no visible key must have LSE = -inf"
+    err = np.abs(g - eo)
+    half_ulp = 0.0 if out_f32 else np.where(
+        np.abs(eo) > 0, np.exp2(np.floor(np.log2(np.maximum(np.abs(eo), 1e-300))) - 8), 0.0)
+    bound = (2.0 ** -4 + n[None, None, :, None] * 2.0 ** -16) * vmax + half_ulp + 1e-6 * (1 + np.abs(eo))
+    ratio = float((err / bound).max())
+    lerr = np.abs(gl[live] - else_[live])
+    lbound = 1e-4 + np.broadcast_to(n[None, None, :], live.shape)[live] * 2.0 ** -24
+    log("  %s O max|err| %.3e mean|err| %.3e (max err/bound %.3f)  LSE max|err| %.3e" % (
+        name, err.max(), err.mean(), ratio, lerr.max(initial=0)))
+    mean_bar = 1.25 * (float(expect.mean()) + float(np.mean(half_ulp)))
+    log("    mean|err| %.3e against the expected %.3e (bar %.3e)" % (err.mean(), expect.mean(), mean_bar))
+    assert ratio <= 1.0, "%s: O error beyond the derived e4m3 bound" % name
+    assert float(err.mean()) <= mean_bar, "%s: O mean-abs error %.3e > %.3e" % (name, err.mean(), mean_bar)
+    assert bool((lerr <= lbound).all()), "%s: LSE error %.3e" % (name, lerr.max())
+
+
+CASES = [
+    # B, H, N, Nk, causal
+    (2, 3, 300, 300, True), (2, 3, 300, 300, False), (1, 2, 1, 1, True), (1, 2, 65, 65, True),
+    (1, 2, 129, 129, False), (2, 2, 1000, 1000, True), (1, 3, 100, 777, True),
+    (1, 3, 500, 200, True), (2, 8, 1024, 1024, False), (2, 8, 1024, 1024, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["%dx%dx%dx%d_c%d" % c for c in CASES])
+def test_fp8_forward_matches_oracle_on_dequantized_inputs(gpu_lib, case):
+    B, H, N, Nk, causal = case
+    w = Workload("fp8", B, H, N, 128, "bf16", causal=causal, seed=90 + N + Nk)
+    log("case %s" % (case,))
+    q8, k8, v8, dq, dk, dv = workloads.draw_fp8(w, Nk)
+    qd, kd, vd = (workloads.dequantize(x, s) for x, s in ((q8, dq), (k8, dk), (v8, dv)))
+    eo, el = oracle.fwd(qd, kd, vd, w.softmax_scale, causal)
+    expect = expected_abs_error(qd, kd, vd, w.softmax_scale, causal, el)
+    vmax, n = visible_vmax(vd.numpy(), N, causal)
+    dev = "cuda"
+    args = [t.to(dev) for t in (q8, k8, v8, dq, dk, dv)]
+    for out_f32 in (False, True):
+        o, lse = gpu_lib.fwd_fp8(*args, scale=w.softmax_scale, causal=causal, out_f32=out_f32)
+        torch.cuda.synchronize()
+        assert o.dtype == (torch.float32 if out_f32 else torch.bfloat16)
+        check("out_f32=%d" % out_f32, o, lse, eo, el, vmax, n, out_f32, expect)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_forward_full_size_every_head(gpu_lib, causal):
+    """1 x 32 x 4096 x 128 (the long causal forward's shape; 512 units of
+    256 rows: the eight-wavefront layout), every element of every head."""
+    w = Workload("fp8_full", 1, 32, 4096, 128, "bf16", causal=causal, seed=4)
+    log("case fp8 1x32x4096 causal=%d" % causal)
+    q8, k8, v8, dq, dk, dv = workloads.draw_fp8(w)
+    qd, kd, vd = (workloads.dequantize(x, s) for x, s in ((q8, dq), (k8, dk), (v8, dv)))
+    eo, el = oracle.fwd(qd, kd, vd, w.softmax_scale, causal)
+    expect = expected_abs_error(qd, kd, vd, w.softmax_scale, causal, el)
+    vmax, n = visible_vmax(vd.numpy(), w.N, causal)
+    o, lse = gpu_lib.fwd_fp8(*[t.to("cuda") for t in (q8, k8, v8, dq, dk, dv)],
+                             scale=w.softmax_scale, causal=causal)
+    torch.cuda.synchronize()
+    check("bf16 out", o, lse, eo, el, vmax, n, False, expect)
+
+
+def test_fp8_single_key_returns_value(gpu_lib):
+    """N = 1: one probability, exactly 1 (2^6 in e4m3 is exact), so O is the
+    dequantized value row (to the output's rounding) and LSE = scale q.k."""
+    w = Workload("fp8_n1", 3, 4, 1, 128, "bf16", causal=True, seed=5)
+    q8, k8, v8, dq, dk, dv = workloads.draw_fp8(w)
+    o, lse = gpu_lib.fwd_fp8(*[t.to("cuda") for t in (q8, k8, v8, dq, dk, dv)],
+                             scale=w.softmax_scale, causal=True, out_f32=True)
+    vd = workloads.dequantize(v8, dv)
+    assert float((o.cpu().double() - vd).abs().max()) <= 1e-6 * float(vd.abs().max())
+    ref = w.softmax_scale * (workloads.dequantize(q8, dq) * workloads.dequantize(k8, dk)).sum(-1)
+    assert float((lse.cpu().double() - ref).abs().max()) < 1e-4
+
+
+def test_fp8_rejections(gpu_lib):
+    fa = gpu_lib
+    lib = fa.load()
+    import ctypes
+    x = torch.zeros((1, 1, 16, 128), dtype=torch.float8_e4m3fn, device="cuda")
+    s = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fa.fwd_fp8(x.view(torch.uint8), x, x, s, s, s)
+    p = fa.make_params(1, 1, 16, 64, fa.FP8_E4M3)
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.fa_fwd_fp8(ctypes.byref(p), *([fake] * 8), None) == fa.FA_EUNSUPPORTED
+    p = fa.make_params(1, 1, 16, 128, fa.FP8_E4M3, dropout_p=0.1)
+    assert lib.fa_fwd_fp8(ctypes.byref(p), *([fake] * 8), None) == fa.FA_EUNSUPPORTED
+    p = fa.make_params(1, 1, 16, 128, fa.BF16)
+    assert lib.fa_fwd_fp8(ctypes.byref(p), *([fake] * 8), None) == fa.FA_EINVAL
+    p = fa.make_params(1, 1, 16, 128, fa.FP8_E4M3)
+    assert lib.fa_fwd(ctypes.byref(p), *([fake] * 5), None) == fa.FA_EUNSUPPORTED

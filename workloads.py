@@ -84,6 +84,40 @@ def draw_cross(w: Workload, Nk: int, with_dout: bool = False):
     return tuple(out)
 
 
+E4M3_MAX = 448.0   # largest finite OCP e4m3 value
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Per-(b, h) e4m3 quantization of an fp32 [B,H,N,d] draw: descale =
+    max|x| / 448 over the head (float32), x8 = RNE(x / descale) in e4m3.
+    Returns (x8 torch.float8_e4m3fn, descale float32 [B,H]); the attention
+    inputs are x8 * descale."""
+    amax = x.abs().amax(dim=(2, 3)).to(torch.float32)
+    descale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    x8 = (x / descale[:, :, None, None]).to(torch.float8_e4m3fn)
+    return x8, descale
+
+
+def draw_fp8(w: Workload, Nk: int | None = None):
+    """q8, k8, v8 (torch.float8_e4m3fn) and their float32 [B,H] descale
+    factors: N(0,1) draws in the order q, k, v from a CPU generator seeded
+    with ``w.seed`` (k and v with Nk rows when given), each head quantized
+    with quantize_e4m3."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    nk = w.N if Nk is None else Nk
+    q = torch.randn((w.B, w.H, w.N, w.d), dtype=torch.float32, generator=g)
+    k = torch.randn((w.B, w.H, nk, w.d), dtype=torch.float32, generator=g)
+    v = torch.randn((w.B, w.H, nk, w.d), dtype=torch.float32, generator=g)
+    (q8, dq), (k8, dk), (v8, dv) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    return q8, k8, v8, dq, dk, dv
+
+
+def dequantize(x8: torch.Tensor, descale: torch.Tensor) -> torch.Tensor:
+    """float64 values of an e4m3 tensor times its per-(b, h) descale (exact:
+    a 4-bit significand times a 24-bit one fits in float64)."""
+    return x8.to(torch.float64) * descale.to(torch.float64)[:, :, None, None]
+
+
 DROPOUT_SEED = 0x5EED000000000005
 
 # The five workloads the targets are stated on (shapes, dtypes, modes).
