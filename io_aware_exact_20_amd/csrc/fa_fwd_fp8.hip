@@ -24,10 +24,10 @@
 // 2^2, so every probability is at most 4 and P * 2^6 <= 256 stays below the
 // e4m3 maximum (448).
 //
-// Layout: as in the 16-bit two-wavefront forward -- 32 query rows per
-// wavefront, two wavefronts per SIMD in opposite phases (eight wavefronts
-// of 256 rows, one workgroup per CU; or four of 128 rows and two workgroups
-// per CU for small problems), 64-key tiles in LDS by direct buffer loads.
+// Layout: as in the 16-bit forward -- 32 query rows per wavefront, four
+// wavefronts (128 rows) per workgroup and two workgroups per CU, so the two
+// wavefronts of a SIMD come from different workgroups; 64-key tiles in LDS
+// by direct buffer loads, two K and two V buffers, loaded one step ahead.
 // A tile row is 128 bytes (d = 128), stored with the XOR swizzle of 128-byte
 // rows.  K operands (32 bytes of a key row per lane) are two 16-byte reads;
 // V^T operands are four ds_read_b64_tr_b8 reads, addressed so that byte p of
@@ -42,14 +42,13 @@ namespace fa {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-template <bool W4>
 struct FwdFp8Tile {
     static constexpr int D = 128;
-    static constexpr int NW = W4 ? 4 : 8;
-    static constexpr int WG_PER_CU = W4 ? 2 : 1;
+    static constexpr int NW = 4;
+    static constexpr int WG_PER_CU = 2;
     static constexpr int BQ = 32 * NW;            // query rows per workgroup
     static constexpr int BC = 64;                 // keys per tile (two 32-key blocks)
-    static constexpr int NBUF = W4 ? 2 : 3;       // K and V buffers each
+    static constexpr int NBUF = 2;                // K and V buffers each
     static constexpr int RB = D;                  // bytes per tile row
     static constexpr int TILE_BYTES = BC * RB;    // 8 KB
     static constexpr int CHUNK_BYTES = kWave * 16;
@@ -60,8 +59,8 @@ struct FwdFp8Tile {
     static constexpr int THREADS = NW * kWave;
 };
 
-template <bool W4> constexpr int kF8Threads = FwdFp8Tile<W4>::THREADS;
-template <bool W4> constexpr int kF8WgPerCu = FwdFp8Tile<W4>::WG_PER_CU;
+constexpr int kF8Threads = FwdFp8Tile::THREADS;
+constexpr int kF8WgPerCu = FwdFp8Tile::WG_PER_CU;
 
 // Rescale threshold (log2 units) and the power of two the probabilities are
 // scaled by before rounding to e4m3 (4 * 2^6 = 256 < 448).
@@ -83,22 +82,19 @@ __device__ __forceinline__ void mma8(f32x16 &acc, const i32x8 &a, const i32x8 &b
     acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
 }
 
-template <bool CAUSAL, bool W4>
-__global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel(const FwdArgs a) {
-    using TL = FwdFp8Tile<W4>;
+template <bool CAUSAL>
+__global__ void __launch_bounds__(kF8Threads, kF8WgPerCu) fwd_fp8_kernel(const FwdArgs a) {
+    using TL = FwdFp8Tile;
     constexpr int D = TL::D, BQ = TL::BQ, BC = TL::BC, NW = TL::NW, NBUF = TL::NBUF;
     constexpr int TB = TL::TILE_BYTES, CB = TL::CHUNK_BYTES, RPC = TL::RPC, LPT = TL::LPT;
-    constexpr int LOADS = TL::LOADS;
     constexpr float kNegInf = -__builtin_huge_valf();
 
     __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], vs0[TB], vs1[TB];
-    __shared__ __attribute__((aligned(1024))) char ks2[NBUF > 2 ? TB : 16], vs2[NBUF > 2 ? TB : 16];
+    static_assert(NBUF == 2, "two K and two V buffers");
 
     const int lane = (int)lane_in_wave();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lq = lane & 31, g = lane >> 5;
-    const int order = NW == 8 ? wave >> 2 : 0;       // 0: matrix phase first
-    const int rblk = NW == 8 ? (order == 0 ? (wave & 3) : 7 - (wave & 3)) : wave;
 
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
@@ -112,9 +108,10 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
     const uint8_t *__restrict__ V = reinterpret_cast<const uint8_t *>(a.v) + head_kv;
 
     const int q0 = (int)qb * BQ;
-    const int q0w = q0 + 32 * rblk;
+    const int q0w = q0 + 32 * wave;
     const int qrow = q0w + lq;
-    const int64_t off = (int64_t)Nk - N;
+    // causal: query i sees keys j <= i + off (all index arithmetic fits in 32 bits: N, Nk < 2^31)
+    const int off = Nk - N;
 
     // exponent scale of the scores (log2 units), and the output factor
     const float sl2 = a.scale_log2 * a.descale_q[bh] * a.descale_k[bh];
@@ -167,8 +164,8 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
     }
     const uint32_t head_bytes = (uint32_t)Nk * D;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
-    auto kbuf = [&](int m) { return m == 0 ? (lds_char *)ks0 : m == 1 ? (lds_char *)ks1 : (lds_char *)ks2; };
-    auto vbuf = [&](int m) { return m == 0 ? (lds_char *)vs0 : m == 1 ? (lds_char *)vs1 : (lds_char *)vs2; };
+    auto kbuf = [&](int m) { return m == 0 ? (lds_char *)ks0 : (lds_char *)ks1; };
+    auto vbuf = [&](int m) { return m == 0 ? (lds_char *)vs0 : (lds_char *)vs1; };
     auto load_kv = [&](int tk, int kbm, int tv, int vbm) {
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
@@ -178,24 +175,26 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
         }
     };
 
-    auto tiles_to = [&](int64_t end) {
+    // (q0 + BQ + off and q0w + 32 + off stay below N + BQ + Nk; clamped by Nk first)
+    auto tiles_to = [&](int end) {
         end = end < Nk ? end : Nk;
-        return end > 0 ? (int)((end + BC - 1) / BC) : 0;
+        return end > 0 ? (end + BC - 1) / BC : 0;
     };
-    const int NT = tiles_to(CAUSAL ? (int64_t)q0 + BQ + off : (int64_t)Nk);
-    const int Tw = q0w < N ? tiles_to(CAUSAL ? (int64_t)q0w + 32 + off : (int64_t)Nk) : 0;
+    const int NT = tiles_to(CAUSAL ? (q0 + BQ < N ? q0 + BQ : N) + off : Nk);
+    const int Tw = q0w < N ? tiles_to(CAUSAL ? (q0w + 32 < N ? q0w + 32 : N) + off : Nk) : 0;
+    const int edge_k = CAUSAL ? q0w + off : Nk;   // tiles reaching past this key need masks
 
     auto is_edge = [&](int t) {
-        const int64_t k0 = (int64_t)t * BC;
-        return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > q0w + off);
+        const int k0 = t * BC;
+        return (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > edge_k);
     };
     // Register r of key block kb holds key k0 + 4g + 8(r/4) + r%4.
     auto apply_mask = [&](f32x16 &s, int t, int kb) {
         const int k0 = t * BC + 32 * kb;
         int lim = Nk - 1 - (k0 + 4 * g);
         if (CAUSAL) {
-            const int64_t c = (int64_t)qrow + off - (k0 + 4 * g);
-            lim = c < lim ? (int)(c > -64 ? c : -64) : lim;
+            const int c = qrow + off - (k0 + 4 * g);
+            lim = c < lim ? (c > -64 ? c : -64) : lim;
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -260,8 +259,8 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
     auto mat_phase = [&](auto m_c) {
         constexpr int M = decltype(m_c)::value;
         constexpr int MK = (M + 1) % NBUF;
-        const lds_char *kb_ = MK == 0 ? (lds_char *)ks0 : MK == 1 ? (lds_char *)ks1 : (lds_char *)ks2;
-        const lds_char *vb = M == 0 ? (lds_char *)vs0 : M == 1 ? (lds_char *)vs1 : (lds_char *)vs2;
+        const lds_char *kb_ = MK == 0 ? (lds_char *)ks0 : (lds_char *)ks1;
+        const lds_char *vb = M == 0 ? (lds_char *)vs0 : (lds_char *)vs1;
         // S product j: key block j / 2, chunk j % 2 of d.
         auto kfrag = [&](int j) {
             const lds_char *base = kb_ + (j / 2) * 32 * 128;
@@ -303,18 +302,18 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // Loads run NBUF - 1 steps ahead (see the 16-bit forward): step t brings
-    // K_{t+1+NBUF} and V_{t+NBUF}; the end of a step waits by count for the
-    // previous step's loads only, then a bare barrier.
+    // Loads run one step ahead (as in the 16-bit forward): the end of step
+    // t waits for every load in flight, passes a bare barrier and brings
+    // K_{t+3} and V_{t+2}.
     auto end_step = [&](auto m_c, int t) {
         constexpr int M = decltype(m_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0070 | (LOADS * (NBUF - 2)));   // vmcnt(LOADS (NBUF-2)), lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_kv(t + 1 + NBUF, (M + 1) % NBUF, t + NBUF, M);
+        load_kv(t + 3, (M + 1) % 2, t + 2, M);
     };
     load_kv(0, 0, 0, 0);
     load_kv(1, 1, 0, 0);
@@ -337,30 +336,25 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 2; u <= NBUF; ++u) load_kv(u, u % NBUF, u - 1, (u - 1) % NBUF);
+    load_kv(2, 0, 1, 1);   // K_2, V_1
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     auto step = [&](auto m_c, int t) {
         constexpr int M = decltype(m_c)::value;
         vec_phase(t);
-        if (order == 0 && t > 0) end_step(std::integral_constant<int, (M + NBUF - 1) % NBUF>{}, t - 1);
+        if (t > 0) end_step(std::integral_constant<int, (M + 1) % 2>{}, t - 1);
         mat_phase(m_c);
-        if (order != 0) end_step(m_c, t);
     };
     auto end_step_rt = [&](int t) {
-        const int m = t % NBUF;
-        if (m == 0) end_step(I0{}, t);
-        else if (m == 1) end_step(I1{}, t);
-        else end_step(std::integral_constant<int, (NBUF > 2 ? 2 : 1)>{}, t);
+        if (t % 2 == 0) end_step(I0{}, t);
+        else end_step(I1{}, t);
     };
-    for (int t = 0; t < Tw; t += NBUF) {
+    for (int t = 0; t < Tw; t += 2) {
         step(I0{}, t);
         if (t + 1 < Tw) step(I1{}, t + 1);
-        if (NBUF > 2 && t + 2 < Tw) step(std::integral_constant<int, (NBUF > 2 ? 2 : 0)>{}, t + 2);
     }
-    if (order == 0 && Tw > 0) end_step_rt(Tw - 1);
+    if (Tw > 0) end_step_rt(Tw - 1);
     for (int t = Tw; t < NT; ++t) end_step_rt(t);
     __builtin_amdgcn_s_waitcnt(0);
 
@@ -389,24 +383,21 @@ __global__ void __launch_bounds__(kF8Threads<W4>, kF8WgPerCu<W4>) fwd_fp8_kernel
     }
 }
 
-template <bool CAUSAL, bool W4>
+template <bool CAUSAL>
 static hipError_t launch_fwd_fp8_k(const FwdArgs &a, hipStream_t stream) {
-    using TL = FwdFp8Tile<W4>;
+    using TL = FwdFp8Tile;
     const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
     const int64_t units = a.B * a.H * nqb;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     FwdArgs b = a;
     b.group = unit_group(a.B * a.H, nqb, TL::WG_PER_CU);
-    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, W4>), dim3((unsigned)units), dim3(TL::THREADS), 0, stream, b);
+    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3((unsigned)units), dim3(TL::THREADS), 0, stream, b);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_fp8(int d, bool causal, const FwdArgs &a, hipStream_t stream) {
     if (d != 128 || a.kv_splits != 1) return hipErrorInvalidValue;
-    // 256-row units unless that gives fewer than two per CU (as the 16-bit forward).
-    const bool w4 = a.B * a.H * ((a.N + 255) / 256) < 512;
-    if (causal) return w4 ? launch_fwd_fp8_k<true, true>(a, stream) : launch_fwd_fp8_k<true, false>(a, stream);
-    return w4 ? launch_fwd_fp8_k<false, true>(a, stream) : launch_fwd_fp8_k<false, false>(a, stream);
+    return causal ? launch_fwd_fp8_k<true>(a, stream) : launch_fwd_fp8_k<false>(a, stream);
 }
 
 }  // namespace fa

@@ -18,14 +18,12 @@
 // vector ALU (the overlap of softmax with the matrix products that the
 // flash-attention-4 page describes, applied to wavefronts sharing a SIMD;
 // within one wavefront a product hides only a few vector instructions).
-// Without dropout a workgroup has eight wavefronts (256 rows, 64-key
-// steps): wavefronts 0-3 run matrix then vector phase, 4-7 vector then
-// matrix phase, and the two wavefronts on one SIMD (w and w + 4) belong to
-// different halves (and own row blocks w and 7 - w).  With dropout a workgroup has four wavefronts (128
-// rows, 32-key steps) and two workgroups share a CU, so the other
-// workgroup's wavefronts run while one waits at its step barrier.
+// A workgroup has four wavefronts (128 rows) and two workgroups share a CU,
+// so the two wavefronts of a SIMD come from different workgroups and one
+// runs while the other waits at its step barrier.  Steps cover 64 keys
+// without dropout and 32 keys with it.
 
-// Layout of the products, as in the other 16-bit forward: scores are
+// Layout of the products: scores are
 // formed transposed, S^T = K Q^T, so a lane owns one query row and sixteen
 // keys of a tile; the rounded scores are directly the B operand of
 // O^T += V^T P^T; V^T comes from the row-major LDS tile through
@@ -38,24 +36,23 @@
 
 namespace fa {
 
-template <typename T, int D, bool DROPOUT, bool W4>
+template <typename T, int D, bool DROPOUT>
 struct FwdPPTile {
-    // W4 = false: eight wavefronts, two per SIMD in opposite phases.
-    // W4 = true: four wavefronts and two workgroups per CU (the second
-    // workgroup's wavefronts fill the SIMDs while one workgroup waits at its
-    // step barrier); used with dropout (measured 9 % faster than eight
-    // wavefronts there) and for problems with few query blocks (twice as
-    // many, smaller work units).
-    static constexpr int NW = W4 ? 4 : 8;
-    static constexpr int WG_PER_CU = W4 ? 2 : 1;
+    // Four wavefronts and two workgroups per CU: the two wavefronts of a SIMD
+    // come from different workgroups, so one workgroup's wavefronts run while
+    // the other's wait at their step barrier (measured faster than eight
+    // wavefronts of one workgroup in opposite phases at every size: 9 % with
+    // dropout, 1-2 % without).
+    static constexpr int NW = 4;
+    static constexpr int WG_PER_CU = 2;
     static constexpr int BQ = 32 * NW;                    // query rows per workgroup
     // 32-key blocks per tile: two without dropout (one barrier per 64 keys);
     // one with it (two measured no faster there and need the vector phase
     // inlined by force to stay out of scratch memory).
     static constexpr int NKB = DROPOUT ? 1 : 2;
-    // K and V buffers each; tiles are loaded NBUF - 1 steps ahead (two
-    // buffers when two workgroups share the LDS).
-    static constexpr int NBUF = W4 ? 2 : 3;
+    // K and V buffers each (two workgroups share the LDS); tiles are loaded
+    // one step ahead.
+    static constexpr int NBUF = 2;
     static constexpr int BC = 32 * NKB;                   // keys per tile
     static constexpr int THREADS = NW * kWave;
     static constexpr int TILE_BYTES = BC * D * 2;         // one K or V tile
@@ -65,15 +62,15 @@ struct FwdPPTile {
 };
 
 // Launch bounds (single template arguments: the attribute macro splits at commas).
-template <bool W4> constexpr int kPPThreads = FwdPPTile<bf16, 128, false, W4>::THREADS;
-template <bool W4> constexpr int kPPWgPerCu = FwdPPTile<bf16, 128, false, W4>::WG_PER_CU;
+constexpr int kPPThreads = FwdPPTile<bf16, 128, false>::THREADS;
+constexpr int kPPWgPerCu = FwdPPTile<bf16, 128, false>::WG_PER_CU;
 
 // Lazy-rescale threshold (log2 units), as in the other forward kernels.
 constexpr float kPPRescaleLog2 = 8.0f;
 
-template <typename T, int D, bool CAUSAL, bool DROPOUT, bool W4>
-__global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(const FwdArgs a) {
-    using TL = FwdPPTile<T, D, DROPOUT, W4>;
+template <typename T, int D, bool CAUSAL, bool DROPOUT>
+__global__ void __launch_bounds__(kPPThreads, kPPWgPerCu) fwd_pp_kernel(const FwdArgs a) {
+    using TL = FwdPPTile<T, D, DROPOUT>;
     using SW = Swz<D>;
     constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW, NKB = TL::NKB, NBUF = TL::NBUF;
     constexpr int TB = TL::TILE_BYTES, CB = TL::CHUNK_BYTES, CHUNKS = TL::CHUNKS, LOADS = TL::LOADS;
@@ -85,19 +82,13 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
     static_assert(D == 64 || D == 128, "tile plan for d = 64 and 128");
     static_assert(2 * NDB == NDC, "one V^T product per K product");
 
-    // LDS: K tile t in buffer t % NBUF, V tile t in buffer t % NBUF (the
-    // third buffers are unused when NBUF = 2).
+    // LDS: K tile t in buffer t % 2, V tile t in buffer t % 2.
     __shared__ __attribute__((aligned(1024))) char ks0[TB], ks1[TB], vs0[TB], vs1[TB];
-    __shared__ __attribute__((aligned(1024))) char ks2[NBUF > 2 ? TB : 16], vs2[NBUF > 2 ? TB : 16];
+    static_assert(NBUF == 2, "two K and two V buffers");
 
     const int lane = (int)lane_in_wave();
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lq = lane & 31, g = lane >> 5;
-    const int order = NW == 8 ? wave >> 2 : 0;       // 0: matrix phase first
-    // Eight wavefronts: waves w and w + 4 share a SIMD and own row blocks w
-    // and 7 - w, so that on the causal diagonal every SIMD pairs a long and
-    // a short wavefront (the long one has the SIMD to itself at the end).
-    const int rblk = NW == 8 ? (order == 0 ? (wave & 3) : 7 - (wave & 3)) : wave;
 
     const int64_t BH = a.B * a.H;
     const int64_t nqb = (a.N + BQ - 1) / BQ;
@@ -114,7 +105,7 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
     const uint32_t b_idx = (uint32_t)(bh / a.H), h_idx = (uint32_t)(bh % a.H);
 
     const int q0 = (int)qb * BQ;
-    const int q0w = q0 + 32 * rblk;                    // first query row of this wavefront
+    const int q0w = q0 + 32 * wave;                    // first query row of this wavefront
     const int qrow = q0w + lq;                         // this lane's query row
     const int klo = split * a.kv_chunk;
     const int khi = (int)((int64_t)klo + a.kv_chunk < (int64_t)Nk ? klo + a.kv_chunk : Nk);
@@ -159,8 +150,8 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
     // Buffers by tile index mod 3 (compile-time wherever tiles are read, so
     // that the compiler can tell the loads into one buffer from reads of
     // another).
-    auto kbuf = [&](int m) { return m == 0 ? (lds_char *)ks0 : m == 1 ? (lds_char *)ks1 : (lds_char *)ks2; };
-    auto vbuf = [&](int m) { return m == 0 ? (lds_char *)vs0 : m == 1 ? (lds_char *)vs1 : (lds_char *)vs2; };
+    auto kbuf = [&](int m) { return m == 0 ? (lds_char *)ks0 : (lds_char *)ks1; };
+    auto vbuf = [&](int m) { return m == 0 ? (lds_char *)vs0 : (lds_char *)vs1; };
     // This wavefront's share of the loads of K tile tk and V tile tv into
     // K buffer kbm and V buffer vbm.
     auto load_kv = [&](int tk, int kbm, int tv, int vbm) {
@@ -289,8 +280,8 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
         constexpr int M = decltype(m_c)::value;
         constexpr int NJ = NKB * NDC;   // products of each kind (S: key block x d chunk; O: key chunk x d block)
         constexpr int MK = (M + 1) % NBUF;
-        const lds_char *kb_ = MK == 0 ? (lds_char *)ks0 : MK == 1 ? (lds_char *)ks1 : (lds_char *)ks2;  // K_{t+1}
-        const lds_char *vb = M == 0 ? (lds_char *)vs0 : M == 1 ? (lds_char *)vs1 : (lds_char *)vs2;      // V_t
+        const lds_char *kb_ = MK == 0 ? (lds_char *)ks0 : (lds_char *)ks1;  // K_{t+1}
+        const lds_char *vb = M == 0 ? (lds_char *)vs0 : (lds_char *)vs1;      // V_t
         // S product j: key block j / NDC, contraction chunk j % NDC.
         auto kfrag = [&](int j) { return lds_frag<T>(kb_ + (j / NDC) * 32 * RB + koff[j % NDC]); };
         // O product j: key chunk (16 keys) j / NDB, output block j % NDB.
@@ -329,32 +320,28 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
         __builtin_amdgcn_s_setprio(0);
     };
 
-    // Loads run NBUF - 1 steps ahead: step t brings K_{t+NBUF} and
-    // V_{t+NBUF-1} (into the buffers of K_t and V_{t-1}, free since the end
-    // of step t-1), and the end of step t waits for every load but this
-    // step's own when NBUF = 3 (the loads of step t-1 are K_{t+2}, V_{t+1},
-    // which step t+1 reads), for all of them when NBUF = 2.  Loads past the
-    // end read zeros (or keys no row uses), so every step issues the same
-    // number and the count is exact.  The barrier is the bare instruction after explicit counts (a
-    // workgroup fence would wait for every load in flight); no memory
-    // operation is moved across it (scheduling barriers on both sides, and
-    // the hardware barrier is an unmodelled side effect for the compiler).
-    // (The buffer indices of the loads are compile-time constants too, so
-    // that the compiler sees which buffer each direct load writes.)
-    auto end_step = [&](auto m_c, int t) {   // m_c: t % NBUF
+    // Loads run one step ahead: the end of step t brings K_{t+3} and V_{t+2}
+    // (into the buffers of K_{t+1} and V_t, read for the last time in step
+    // t) after waiting for every load in flight (K_{t+2}, V_{t+1}, which step
+    // t+1 reads).  Loads past the end read zeros (or keys no row uses), so
+    // every step issues the same number.  The barrier is the bare
+    // instruction after explicit counts; no memory operation is moved across
+    // it (scheduling barriers on both sides, and the hardware barrier is an
+    // unmodelled side effect for the compiler).  (The buffer indices of the
+    // loads are compile-time constants too, so that the compiler sees which
+    // buffer each direct load writes.)
+    auto end_step = [&](auto m_c, int t) {   // m_c: t % 2
         constexpr int M = decltype(m_c)::value;
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");   // no memory operation crosses this point in the IR either
-        // vmcnt(LOADS (NBUF - 2)), lgkmcnt(0)
-        __builtin_amdgcn_s_waitcnt(0x0070 | (LOADS * (NBUF - 2)));
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_kv(t + 1 + NBUF, (M + 1) % NBUF, t + NBUF, M);   // K_{t+1+NBUF}, V_{t+NBUF}
+        load_kv(t + 3, (M + 1) % 2, t + 2, M);   // K_{t+3}, V_{t+2}
     };
-    // ---- prologue: K_0, K_1, V_0, then S of tile 0; then the loads of the
-    // steps before step 0 and of step 0 itself (K_2, V_1, and with three
-    // buffers K_3, V_2).
+    // ---- prologue: K_0, K_1, V_0, then S of tile 0; then the loads of step
+    // 0 (K_2, V_1).
     load_kv(0, 0, 0, 0);
     load_kv(1, 1, 0, 0);   // (V_0 loaded twice: same data, same place)
 #pragma unroll
@@ -370,38 +357,32 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
         }
     }
     __syncthreads();   // K buffer 0 is refilled before step 0
-#pragma unroll
-    for (int u = 2; u <= NBUF; ++u) load_kv(u, u % NBUF, u - 1, (u - 1) % NBUF);   // K_u, V_{u-1}
+    load_kv(2, 0, 1, 1);   // K_2, V_1
 
-    // ---- steps.  Both halves run the phase sequence vec(0) mat(0) vec(1)
-    // mat(1) ... mat(Tw-1); step t (one barrier) is [vec(t) mat(t)] for the
-    // second half and [mat(t) vec(t+1)] for the first, so the two
-    // wavefronts of a SIMD are in opposite phases.  Step t reads K_{t+1} and
-    // V_t in both.  Three steps per trip, so buffer indices are constants.
-    // Wavefronts past their last tile keep the loads and barriers of the
-    // workgroup going.
+    // ---- steps.  Every wavefront runs the phase sequence vec(0) mat(0)
+    // vec(1) mat(1) ... mat(Tw-1), with the barrier of step t-1 between
+    // vec(t) and mat(t); the other wavefront on its SIMD belongs to the other
+    // workgroup on the CU, so whichever is not waiting keeps the SIMD busy.
+    // Step t reads K_{t+1} and V_t.  Two steps per trip, so buffer indices
+    // are constants.  Wavefronts past their last tile keep the loads and
+    // barriers of the workgroup going.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
     auto step = [&](auto m_c, int t) {
         constexpr int M = decltype(m_c)::value;
         vec_phase(t);
-        if (order == 0 && t > 0) end_step(std::integral_constant<int, (M + NBUF - 1) % NBUF>{}, t - 1);
+        if (t > 0) end_step(std::integral_constant<int, (M + 1) % 2>{}, t - 1);
         mat_phase(m_c);
-        if (order != 0) end_step(m_c, t);
     };
-    auto end_step_rt = [&](int t) {   // run-time t % NBUF (no LDS reads follow)
-        const int m = t % NBUF;
-        if (m == 0) end_step(I0{}, t);
-        else if (m == 1) end_step(I1{}, t);
-        else end_step(std::integral_constant<int, (NBUF > 2 ? 2 : 1)>{}, t);
+    auto end_step_rt = [&](int t) {   // run-time t % 2 (no LDS reads follow)
+        if (t % 2 == 0) end_step(I0{}, t);
+        else end_step(I1{}, t);
     };
-    for (int t = 0; t < Tw; t += NBUF) {
+    for (int t = 0; t < Tw; t += 2) {
         step(I0{}, t);
         if (t + 1 < Tw) step(I1{}, t + 1);
-        if (NBUF > 2 && t + 2 < Tw) step(std::integral_constant<int, (NBUF > 2 ? 2 : 0)>{}, t + 2);
     }
-    if (order == 0 && Tw > 0) end_step_rt(Tw - 1);
+    if (Tw > 0) end_step_rt(Tw - 1);
     for (int t = Tw; t < NT; ++t) end_step_rt(t);
     __builtin_amdgcn_s_waitcnt(0);   // no load into LDS outlives the workgroup
 
@@ -437,27 +418,23 @@ __global__ void __launch_bounds__(kPPThreads<W4>, kPPWgPerCu<W4>) fwd_pp_kernel(
     }
 }
 
-template <typename T, int D, bool CAUSAL, bool DROPOUT, bool W4>
+template <typename T, int D, bool CAUSAL, bool DROPOUT>
 static hipError_t launch_fwd_pp_k(const FwdArgs &a, hipStream_t stream) {
-    using TL = FwdPPTile<T, D, DROPOUT, W4>;
+    using TL = FwdPPTile<T, D, DROPOUT>;
     const int64_t nqb = (a.N + TL::BQ - 1) / TL::BQ;
     const int64_t units = a.B * a.H * nqb * a.kv_splits;
     if (units > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)units), block(TL::THREADS);
     FwdArgs b = a;
     b.group = unit_group(a.B * a.H, nqb * a.kv_splits, TL::WG_PER_CU);
-    hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL, DROPOUT, W4>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((fwd_pp_kernel<T, D, CAUSAL, DROPOUT>), grid, block, 0, stream, b);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL>
 static hipError_t launch_fwd_pp_c(bool dropout, const FwdArgs &a, hipStream_t stream) {
-    if (dropout) return launch_fwd_pp_k<T, D, CAUSAL, true, true>(a, stream);
-    // Without dropout, 256-row units unless that gives fewer than two per
-    // CU (256 CUs), in which case 128-row units, two workgroups per CU.
-    const int64_t units256 = a.B * a.H * ((a.N + 255) / 256) * a.kv_splits;
-    if (units256 < 512) return launch_fwd_pp_k<T, D, CAUSAL, false, true>(a, stream);
-    return launch_fwd_pp_k<T, D, CAUSAL, false, false>(a, stream);
+    return dropout ? launch_fwd_pp_k<T, D, CAUSAL, true>(a, stream)
+                   : launch_fwd_pp_k<T, D, CAUSAL, false>(a, stream);
 }
 
 template <typename T, int D>

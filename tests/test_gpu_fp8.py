@@ -112,8 +112,8 @@ def test_fp8_forward_matches_oracle_on_dequantized_inputs(gpu_lib, case):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_forward_full_size_every_head(gpu_lib, causal):
-    """1 x 32 x 4096 x 128 (the long causal forward's shape; 512 units of
-    256 rows: the eight-wavefront layout), every element of every head."""
+    """1 x 32 x 4096 x 128 (the long causal forward's shape), every element
+    of every head."""
     w = Workload("fp8_full", 1, 32, 4096, 128, "bf16", causal=causal, seed=4)
     log("case fp8 1x32x4096 causal=%d" % causal)
     q8, k8, v8, dq, dk, dv = workloads.draw_fp8(w)

@@ -336,11 +336,10 @@ def test_long_context_forward_every_head(gpu_lib, name):
 
 
 @pytest.mark.parametrize("dt,causal", [("f16", True), ("f16", False), ("bf16", False)])
-def test_full_size_forward_eight_wavefront_layout(gpu_lib, dt, causal):
-    """1 x 32 x 4096 x 128 without dropout: 512 units of 256 rows, the size
-    at which the forward takes its eight-wavefront layout (64-key steps,
-    three buffers); fp16 inputs and the non-causal case on it, two heads
-    compared element by element."""
+def test_full_size_forward_fp16_and_noncausal(gpu_lib, dt, causal):
+    """1 x 32 x 4096 x 128 without dropout (64-key steps): fp16 inputs
+    causal and not, and the non-causal bf16 case, two heads compared
+    element by element."""
     w = Workload("full8_%s_c%d" % (dt, causal), 1, 32, 4096, 128, dt, causal=causal, seed=41 + causal)
     heads = [(0, 0), (0, 17)]
     log("case %s heads %s" % (w.name, heads))
@@ -521,8 +520,7 @@ def test_tile_boundary_probe_at_full_shape(gpu_lib, p, H):
     """Training shape: V has one-hot columns on 128 keys at tile boundaries,
     so O[:, c] = P~[:, probe_c] and its zero pattern must equal the oracle's
     keep & causal pattern exactly; dO one-hot on the probe rows exposes rows
-    of P~ through dV.  Without dropout, 32 heads: the forward's
-    eight-wavefront layout (64-key steps)."""
+    of P~ through dV.  Without dropout, 32 heads (64-key steps)."""
     w0 = workloads.WORKLOADS["train_dropout"]
     B, N, d = 1, w0.N, w0.d
     w = Workload("probe", B, H, N, d, "bf16", causal=True, dropout_p=p,
