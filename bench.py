@@ -306,7 +306,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--profile-workload", default=None, metavar="NAME",
                     help="only run --warmup + --steps steps of the named workload "
-                         "(%s) and log per-stage times; for profiler runs" % ", ".join(workloads.WORKLOADS))
+                         "(%s) and log per-stage times; for profiler runs.  'fp8:NAME' runs the "
+                         "FP8 forward on that workload's shape (d = 128, no dropout)" % ", ".join(workloads.WORKLOADS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of %d bytes three times (the "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)" % COPY_BYTES)
@@ -331,6 +332,22 @@ def main():
 
     import io_aware_exact_20_amd as fa
     fa.load()
+    if args.profile_workload and args.profile_workload.startswith("fp8:"):
+        w0 = workloads.WORKLOADS[args.profile_workload[4:]]
+        w = workloads.Workload("fp8_" + w0.name, w0.B, w0.H, w0.N, 128, "bf16", causal=w0.causal,
+                               seed=w0.seed)
+        xs = [t.to(dev) for t in workloads.draw_fp8(w)]
+        for _ in range(args.warmup):
+            fa.fwd_fp8(*xs, scale=w.softmax_scale, causal=w.causal)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fa.fwd_fp8(*xs, scale=w.softmax_scale, causal=w.causal)
+        e1.record()
+        torch.cuda.synchronize()
+        log("workload %s: fp8 forward %.4f ms" % (w.name, e0.elapsed_time(e1) / max(1, args.steps)))
+        return
     if args.profile_workload:
         w = workloads.WORKLOADS[args.profile_workload]
         prob = make_problem(fa, w, dev, with_bwd=w.backward)
