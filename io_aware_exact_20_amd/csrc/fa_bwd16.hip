@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
     const uint32_t head_bytes = (uint32_t)Nk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, head_bytes), vrs = make_rsrc(Vg, head_bytes);
     auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
-        buf2lds16(rs, lane_boff, (uint32_t)((t * BC + i * RSTEP) * D * 2),
+        buf2lds16(rs, lane_boff, (uint32_t)(t * BC + i * RSTEP) * (uint32_t)(D * 2),
                   buf + (wave + i * NW) * (kWave * 16));
     };
 

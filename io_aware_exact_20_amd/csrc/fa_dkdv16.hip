@@ -158,7 +158,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         role == 0 ? make_rsrc(a.nl2 + (size_t)bh * (size_t)N, (uint32_t)N * 4)
                   : make_rsrc(a.dvec + (size_t)bh * (size_t)N, (uint32_t)N * 4);
     auto load_tile_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
-        buf2lds16(rs, lane_boff, (uint32_t)(((j0 + t) * BQ + i * RSTEP) * D * 2),
+        buf2lds16(rs, lane_boff, (uint32_t)((j0 + t) * BQ + i * RSTEP) * (uint32_t)(D * 2),
                   buf + (wave + i * NW) * (kWave * 16));
     };
     auto load_rows = [&](int t, lds_char *buf) {   // 64 fp32 rows from the tile's first row

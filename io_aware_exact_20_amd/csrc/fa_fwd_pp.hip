@@ -158,8 +158,9 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu) fwd_pp_kernel(const Fw
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = wave + i * NW;
-            buf2lds16(krs, lboff[i], (uint32_t)((klo + tk * BC) * D * 2), kbuf(kbm) + c * CB);
-            buf2lds16(vrs, lboff[i], (uint32_t)((klo + tv * BC) * D * 2), vbuf(vbm) + c * CB);
+            // (byte offsets of up to 2^31 + 3 tiles: unsigned arithmetic)
+            buf2lds16(krs, lboff[i], (uint32_t)(klo + tk * BC) * (uint32_t)(D * 2), kbuf(kbm) + c * CB);
+            buf2lds16(vrs, lboff[i], (uint32_t)(klo + tv * BC) * (uint32_t)(D * 2), vbuf(vbm) + c * CB);
         }
     };
 

@@ -394,6 +394,121 @@ def test_long_context_65536_sampled_rows(gpu_lib):
         compare("LSE", lse[b, h, rows], elx, w.dtype)
 
 
+# -------------------------------------------- largest head the API accepts
+
+# One head of [MAXN, 128] bf16 is 2^31 - 16384 bytes, the largest the library
+# accepts (it addresses a head with signed 32-bit byte offsets).
+MAXN = 2 ** 23 - 64
+
+
+class Stats:
+    """Running max / mean of |got - exact| over chunks, with compare()'s bars."""
+
+    def __init__(self, name, dtype):
+        self.name, self.dtype, self.mx, self.mx_ex, self.s, self.n = name, dtype, 0.0, 0.0, 0.0, 0
+
+    def add(self, got, exact):
+        g = got.detach().double().cpu().numpy()
+        e = np.asarray(exact)
+        assert np.isfinite(g).all(), "%s has non-finite values" % self.name
+        err = np.abs(g - e)
+        slack = half_ulp(e, got.dtype) if got.dtype != torch.float32 else 0.0
+        self.mx = max(self.mx, float(err.max(initial=0.0)))
+        self.mx_ex = max(self.mx_ex, float((err - slack).max(initial=0.0)))
+        self.s += float(err.sum())
+        self.n += err.size
+
+    def check(self):
+        tmax, tmean = TOL[self.dtype]
+        mean = self.s / max(1, self.n)
+        log("  %-4s max|err| %.3e (less storage %.3e) mean|err| %.3e over %d elements" % (
+            self.name, self.mx, self.mx_ex, mean, self.n))
+        assert self.mx_ex <= tmax and mean <= tmean, self.name
+
+
+@pytest.mark.timeout(900)
+def test_largest_key_head_decoding(gpu_lib):
+    """16 queries over MAXN keys (causal, aligned on the last key): byte
+    offsets into K, V, dK and dV reach 2^31 - 16384.  Forward (one pass and
+    split keys) and backward against the oracle; dK and dV compared on the
+    first, last and evenly spaced key rows."""
+    w = Workload("maxk", 1, 1, 16, 128, "bf16", causal=True, seed=77)
+    log("case 16 queries over %d keys" % MAXN)
+    q, k, v, do = workloads.draw_cross(w, MAXN, with_dout=True)
+    dev = "cuda"
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = gpu_lib.fwd(qd, kd, vd, scale=w.softmax_scale, causal=True)
+    os_, lses = gpu_lib.fwd_splitkv(qd, kd, vd, 64, scale=w.softmax_scale, causal=True)
+    dq, dk, dv = gpu_lib.bwd(qd, kd, vd, o, lse, dod, scale=w.softmax_scale, causal=True)
+    torch.cuda.synchronize()
+    del kd, vd
+    edq, edk, edv, eo, el = oracle.bwd(q, k, v, do, w.softmax_scale, True, 0.0, 0)
+    for name, got, exact in (("O", o, eo), ("LSE", lse, el), ("O", os_, eo), ("LSE", lses, el),
+                             ("dQ", dq, edq)):
+        compare(name, got, exact, "bf16")
+    rows = sorted(set(range(0, 512)) | set(range(MAXN - 512, MAXN)) |
+                  set(np.linspace(0, MAXN - 1, 4096).astype(int).tolist()))
+    for name, got, exact in (("dK", dk, edk), ("dV", dv, edv)):
+        compare(name, got[:, :, rows], exact[:, :, rows], "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_largest_query_head(gpu_lib):
+    """MAXN queries over 64 keys (not causal): byte offsets into Q, O, dO and
+    dQ reach 2^31 - 16384.  Rows are independent here, so the oracle runs
+    over chunks of rows (concurrently: the oracle's C calls release the
+    interpreter lock): O, LSE and dQ compared with the usual bars on the
+    first and last chunks and 512 seeded rows of every other chunk, dK and
+    dV against the sum of every chunk's contributions.
+    Each of the 64 dK, dV rows sums 8.4 million query rows (|dK| reaches a
+    few hundred), so the absolute bars of the target workloads (N <= 65536)
+    measure the accumulation length there, not the method: dK and dV are
+    held to the accuracy of their bf16 matrix-core operands instead --
+    max error <= 2^-7 max|exact|, mean error <= 2^-8 mean|exact| per tensor.
+    An addressing error would show as errors of the order of the values."""
+    w = Workload("maxq", 1, 1, MAXN, 128, "bf16", causal=False, seed=78)
+    log("case %d queries over 64 keys" % MAXN)
+    q, k, v, do = workloads.draw_cross(w, 64, with_dout=True)
+    dev = "cuda"
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o, lse = gpu_lib.fwd(qd, kd, vd, scale=w.softmax_scale)
+    dq, dk, dv = gpu_lib.bwd(qd, kd, vd, o, lse, dod, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    del qd, dod
+    st = {n: Stats(n, "bf16") for n in ("O", "LSE", "dQ")}
+    edk = np.zeros((1, 1, 64, 128))
+    edv = np.zeros((1, 1, 64, 128))
+    step = 1 << 17
+    rng = np.random.default_rng(78)
+    chunks = [(r0, min(MAXN, r0 + step)) for r0 in range(0, MAXN, step)]
+
+    def run_chunk(c):
+        r0, r1 = c
+        return oracle.bwd(q[:, :, r0:r1], k, v, do[:, :, r0:r1], w.softmax_scale, False, 0.0, 0)
+
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
+        for (r0, r1), (cdq, cdk, cdv, co, cl) in zip(chunks, ex.map(run_chunk, chunks)):
+            edk += cdk
+            edv += cdv
+            if r0 == 0 or r1 == MAXN:
+                sel = np.arange(r1 - r0)
+            else:
+                sel = np.sort(rng.choice(r1 - r0, size=512, replace=False))
+            rows = torch.from_numpy(r0 + sel)
+            st["O"].add(o[:, :, rows], co[:, :, sel])
+            st["LSE"].add(lse[:, :, rows], cl[:, :, sel])
+            st["dQ"].add(dq[:, :, rows], cdq[:, :, sel])
+    for s_ in st.values():
+        s_.check()
+    for name, got, exact in (("dK", dk, edk), ("dV", dv, edv)):
+        err = np.abs(got.double().cpu().numpy() - exact)
+        mx, mean = float(np.abs(exact).max()), float(np.abs(exact).mean())
+        log("  %-4s max|err| %.3e (max|x| %.2f) mean|err| %.3e (mean|x| %.2f)" % (
+            name, err.max(), mx, err.mean(), mean))
+        assert float(err.max()) <= 2.0 ** -7 * mx and float(err.mean()) <= 2.0 ** -8 * mean, name
+
+
 # ------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("N", [1, 2, 63, 65, 127, 129, 1000])
