@@ -37,9 +37,11 @@ namespace fa {
 //
 // A hands P over through LDS in fp32 (the register image of its
 // accumulator, lane for lane).  Dropout keep decisions are drawn once per
-// tile, half by each wavefront of the pair, as 16-bit masks in a row-major
-// LDS block; the transposed 16-bit LDS read hands every lane the masks of
-// its own (key, rows) registers, already paired as the products need them.
+// tile, a quarter by A and three quarters by B (A carries the
+// exponentials, so this evens out the vector work of the two), as 16-bit
+// masks in a row-major LDS block; the transposed 16-bit LDS read hands
+// every lane the masks of its own (key, rows) registers, already paired as
+// the products need them.
 // Per 32-row step t:
 //   A: S of tile t+1 | P of tile t (to LDS);  dV += dO^T (keep P) of tile t;
 //   B: dP of tile t | dS of tile t-1;         dK += Q^T dS of tile t-1;
@@ -198,34 +200,39 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         }
     };
 
-    // Keep masks of key block kb of this pair for tile t: lane (row lq,
-    // half g) draws the 16 keys 32kb + 16g .. +15 of its row (two Philox
-    // blocks) and stores them as 16-bit masks.  The draw is staged (counters,
-    // then the 20 block-rounds in order, then the masks): the rounds of tile
-    // s+2 are spread over the second product phase of step s and its masks
-    // are formed and stored during the first phase of step s+1, so no part
-    // of the draw waits at the end of a step.
-    struct MaskDraw { Philox4 c[2]; };
-    auto mask_begin = [&](MaskDraw &m, int t, int kb) {
-        const uint32_t grp = (uint32_t)((kp0 + 32 * kb) >> 3) + 2 * g;
+    // Keep masks of this pair's tile t: its 32 rows x 64 keys are eight
+    // Philox blocks of 8 keys per row (block j: keys 8j .. 8j+7), drawn by
+    // the four lanes of a row -- A lane (row lq, half g) block g, B lane
+    // (row lq, half g) blocks 2 + 3g .. 4 + 3g -- and stored as 16-bit masks.
+    // The draw is staged (counters, then the block-rounds in order, then the
+    // masks): the rounds of tile s+2 are spread over the second product
+    // phase of step s and its masks are formed and stored during the first
+    // phase of step s+1, so no part of the draw waits at the end of a step.
+    constexpr int NBA = 1, NBB = 3;   // blocks per lane: A, B
+    struct MaskDraw { Philox4 c[NBB]; };
+    const int jb0 = role == 0 ? g : 2 + 3 * g;    // first block of this lane
+    auto mask_begin = [&](MaskDraw &m, int t) {
+        const uint32_t grp = (uint32_t)(kp0 >> 3) + (uint32_t)jb0;
         const uint32_t row = (uint32_t)((j0 + t) * BQ + lq);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < NBB; ++h) {
             m.c[h].x[0] = grp + h;
             m.c[h].x[1] = row;
             m.c[h].x[2] = h_idx;
             m.c[h].x[3] = b_idx;
         }
     };
-    // Block-rounds u0 .. u1-1 of 20: unit u is round u/2 of block u%2.  The
+    // Block-rounds u0 .. u1-1 of 10 NB: unit u is round u / NB of block
+    // u % NB (NB = NBA or NBB, a compile-time constant at every call).  The
     // state is pinned afterwards so that the rounds stay in the group that
     // issues them.
-    auto mask_rounds = [&](MaskDraw &m, int u0, int u1) {
+    auto mask_rounds = [&](auto nb_c, MaskDraw &m, int u0, int u1) {
+        constexpr int NB = decltype(nb_c)::value;
 #pragma unroll
-        for (int u = u0; u < u1; ++u) philox_round(m.c[u & 1], u >> 1, a.seed_lo, a.seed_hi);
+        for (int u = u0; u < u1; ++u) philox_round(m.c[u % NB], u / NB, a.seed_lo, a.seed_hi);
         if (u1 > u0) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < NB; ++h)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) pin_vgpr(m.c[h].x[q]);
         }
@@ -233,12 +240,12 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     // Masks of block h of a finished draw: word q of the block holds keys 2q
     // (low half) and 2q + 1 (high half).
     const uint32_t kc2 = keep_cmp_const(a.drop_T);
-    auto mask_end_half = [&](MaskDraw &m, int kb, int slot, int h) {
-        FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + (32 * kb + 16 * g) * 2;
+    auto mask_end_blk = [&](MaskDraw &m, int slot, int h) {
+        FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + 16 * (jb0 + h);
         u32x4 w;
 #pragma unroll
         for (int q = 0; q < 4; ++q) w[q] = keep_mask2(m.c[h].x[q], kc2);
-        *(FA_LDS u32x4 *)(p + 16 * h) = w;
+        *(FA_LDS u32x4 *)p = w;
     };
     MaskDraw pend;   // draw whose masks are stored in the first phase of the next step
     // Per-lane byte offset of the transposed mask read: lane receives the
@@ -254,6 +261,8 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    using CNA = std::integral_constant<int, NBA>;
+    using CNB = std::integral_constant<int, NBB>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     using YES = std::true_type;
@@ -275,12 +284,18 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         for (int c = 0; c < NDC; ++c) pin_agpr(kv[kb][c]);
     if (DROPOUT) {
         MaskDraw m0;                     // tile 0: complete
-        mask_begin(m0, 0, role);
-        mask_rounds(m0, 0, 20);
-        mask_end_half(m0, role, 0, 0);
-        mask_end_half(m0, role, 0, 1);
-        mask_begin(pend, 1, role);       // tile 1: stored during step 0
-        mask_rounds(pend, 0, 20);
+        mask_begin(m0, 0);
+        mask_begin(pend, 1);             // tile 1: stored during step 0
+        if (role == 0) {
+            mask_rounds(CNA{}, m0, 0, 10 * NBA);
+            mask_end_blk(m0, 0, 0);
+            mask_rounds(CNA{}, pend, 0, 10 * NBA);
+        } else {
+            mask_rounds(CNB{}, m0, 0, 10 * NBB);
+#pragma unroll
+            for (int h = 0; h < NBB; ++h) mask_end_blk(m0, 0, h);
+            mask_rounds(CNB{}, pend, 0, 10 * NBB);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -366,23 +381,25 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     pgroup(1, c);
                     ppair(c);
                 }
-                if (DROPOUT && (c == 1 || c == 3)) mask_end_half(pend, 0, R + 1, c >> 1);
+                if (DROPOUT && c == 1) mask_end_blk(pend, R + 1, 0);
                 mma(sn[1], qf[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- phase 2: dV^T += dO^T (keep P) of tile s | keep masks of
-            // tile s+2 (block-rounds, cumulative count before group j: UA[j]).
-            constexpr int UA[9] = {0, 1, 2, 5, 8, 11, 14, 17, 20};
-            constexpr int UA64[5] = {0, 5, 10, 15, 20};
+            // tile s+2 (block-rounds, cumulative count before group j: UA[j];
+            // none in the first groups, which finish P of tile s).
+            constexpr int UA[9] = {0, 0, 0, 1, 2, 4, 6, 8, 10};
+            constexpr int UA64[5] = {0, 1, 4, 7, 10};
+            static_assert(UA[8] == 10 * NBA && UA64[4] == 10 * NBA, "A draws NBA blocks");
             MaskDraw md;
-            if (DROPOUT) mask_begin(md, s + 2, 0);
+            if (DROPOUT) mask_begin(md, s + 2);
 #pragma unroll
             for (int j = 0; j < 2 * NDB; ++j) {
                 const int cc = j / NDB, db = j % NDB;
                 if (j + 2 < 2 * NDB) of[(j + 2) % 3] = ofrag(j + 2);
                 if (DROPOUT) {
-                    if (NDB == 4) mask_rounds(md, UA[j], UA[j + 1]);
-                    else mask_rounds(md, UA64[j], UA64[j + 1]);
+                    if (NDB == 4) mask_rounds(CNA{}, md, UA[j], UA[j + 1]);
+                    else mask_rounds(CNA{}, md, UA64[j], UA64[j + 1]);
                 }
                 if (NDC == 8) {
                     if (j == 0) pgroup(0, 3);
@@ -508,24 +525,28 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 #pragma unroll
                     for (int i = IPG * c; i < IPG * (c + 1); ++i) dsitem(i);
                 }
-                if (DROPOUT && (c == 1 || c == 3)) mask_end_half(pend, 1, R + 1, c >> 1);
+                // masks of the pending draw: blocks 0, 1, 2 after products
+                // c = 1, 3, 5 (d = 128) or 1, 2, 3 (d = 64)
+                if (DROPOUT && (NDC == 8 ? (c & 1) && c < 6 : c >= 1))
+                    mask_end_blk(pend, R + 1, NDC == 8 ? c >> 1 : c - 1);
                 mma(dcur[1], of[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- phase 2: dK^T += Q^T dS of tile s-1 | keep masks of tile
             // s+2 (block-rounds, cumulative count before group j: UB[j]).
-            constexpr int UB[9] = {0, 3, 6, 8, 11, 14, 16, 18, 20};
-            constexpr int UB64[5] = {0, 5, 10, 15, 20};
+            constexpr int UB[9] = {0, 4, 8, 12, 16, 19, 22, 26, 30};
+            constexpr int UB64[5] = {0, 8, 15, 23, 30};
+            static_assert(UB[8] == 10 * NBB && UB64[4] == 10 * NBB, "B draws NBB blocks");
             MaskDraw md;
-            if (DROPOUT) mask_begin(md, s + 2, 1);
+            if (DROPOUT) mask_begin(md, s + 2);
             if (HP) {
 #pragma unroll
                 for (int j = 0; j < 2 * NDB; ++j) {
                     const int cc = j / NDB, db = j % NDB;
                     if (j + 2 < 2 * NDB) qt[(j + 2) % 3] = qfrag(j + 2);
                     if (DROPOUT) {
-                        if (NDB == 4) mask_rounds(md, UB[j], UB[j + 1]);
-                        else mask_rounds(md, UB64[j], UB64[j + 1]);
+                        if (NDB == 4) mask_rounds(CNB{}, md, UB[j], UB[j + 1]);
+                        else mask_rounds(CNB{}, md, UB64[j], UB64[j + 1]);
                     }
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
@@ -540,7 +561,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 }
             }
             if (DROPOUT) {
-                if (!HP) mask_rounds(md, 0, 20);
+                if (!HP) mask_rounds(CNB{}, md, 0, 10 * NBB);
                 pend = md;
             }
             __builtin_amdgcn_s_waitcnt(0);
