@@ -1,5 +1,5 @@
-// Forward of fused exact attention for 16-bit inputs at d = 64 and 128 on
-// gfx950, with two wavefronts per SIMD.
+// Forward of fused exact attention for 16-bit inputs at d = 64, 128 and 256
+// on gfx950, with two wavefronts per SIMD (one at d = 256).
 //
 // The method is the one of the other forward kernels: Q, K, V tiled into
 // on-chip blocks, the online-softmax recurrence (running row maximum,
@@ -22,6 +22,12 @@
 // so the two wavefronts of a SIMD come from different workgroups and one
 // runs while the other waits at its step barrier.  Steps cover 64 keys
 // without dropout and 32 keys with it.
+//
+// At d = 256 the output accumulator (128 registers) and Q (64) leave no room
+// for a second wavefront per SIMD: one workgroup per CU, one wavefront per
+// SIMD, 32-key steps.  There each softmax element costs twice the matrix
+// work of d = 128, so the vector phase is short against the products of
+// its own wavefront.
 
 // Layout of the products: scores are
 // formed transposed, S^T = K Q^T, so a lane owns one query row and sixteen
@@ -44,12 +50,12 @@ struct FwdPPTile {
     // wavefronts of one workgroup in opposite phases at every size: 9 % with
     // dropout, 1-2 % without).
     static constexpr int NW = 4;
-    static constexpr int WG_PER_CU = 2;
+    static constexpr int WG_PER_CU = D == 256 ? 1 : 2;
     static constexpr int BQ = 32 * NW;                    // query rows per workgroup
     // 32-key blocks per tile: two without dropout (one barrier per 64 keys);
     // one with it (two measured no faster there and need the vector phase
     // inlined by force to stay out of scratch memory).
-    static constexpr int NKB = DROPOUT ? 1 : 2;
+    static constexpr int NKB = (DROPOUT || D == 256) ? 1 : 2;
     // K and V buffers each (two workgroups share the LDS); tiles are loaded
     // one step ahead.
     static constexpr int NBUF = 2;
@@ -63,13 +69,16 @@ struct FwdPPTile {
 
 // Launch bounds (single template arguments: the attribute macro splits at commas).
 constexpr int kPPThreads = FwdPPTile<bf16, 128, false>::THREADS;
-constexpr int kPPWgPerCu = FwdPPTile<bf16, 128, false>::WG_PER_CU;
+template <int D>
+constexpr int kPPWgPerCu = D == 256 ? 1 : 2;
+static_assert(kPPWgPerCu<128> == FwdPPTile<bf16, 128, false>::WG_PER_CU &&
+                  kPPWgPerCu<256> == FwdPPTile<bf16, 256, false>::WG_PER_CU, "launch bounds");
 
 // Lazy-rescale threshold (log2 units), as in the other forward kernels.
 constexpr float kPPRescaleLog2 = 8.0f;
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>
-__global__ void __launch_bounds__(kPPThreads, kPPWgPerCu) fwd_pp_kernel(const FwdArgs a) {
+__global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const FwdArgs a) {
     using TL = FwdPPTile<T, D, DROPOUT>;
     using SW = Swz<D>;
     constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW, NKB = TL::NKB, NBUF = TL::NBUF;
@@ -79,7 +88,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu) fwd_pp_kernel(const Fw
     constexpr int NDC = D / 16;       // contraction chunks of S
     constexpr int NDB = D / 32;       // 32-column blocks of O
     constexpr float kNegInf = -__builtin_huge_valf();
-    static_assert(D == 64 || D == 128, "tile plan for d = 64 and 128");
+    static_assert(D == 64 || D == 128 || D == 256, "tile plan for d = 64, 128 and 256");
     static_assert(2 * NDB == NDC, "one V^T product per K product");
 
     // LDS: K tile t in buffer t % 2, V tile t in buffer t % 2.
@@ -446,13 +455,15 @@ static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, h
 
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                          hipStream_t stream) {
-    if (d != 64 && d != 128) return hipErrorInvalidValue;
+    if (d != 64 && d != 128 && d != 256) return hipErrorInvalidValue;
     if (e == Elem::BF16)
         return d == 64 ? launch_fwd_pp_t<bf16, 64>(causal, dropout, a, stream)
-                       : launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream);
+               : d == 128 ? launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream)
+                          : launch_fwd_pp_t<bf16, 256>(causal, dropout, a, stream);
     if (e == Elem::F16)
         return d == 64 ? launch_fwd_pp_t<f16, 64>(causal, dropout, a, stream)
-                       : launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream);
+               : d == 128 ? launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream)
+                          : launch_fwd_pp_t<f16, 256>(causal, dropout, a, stream);
     return hipErrorInvalidValue;
 }
 
