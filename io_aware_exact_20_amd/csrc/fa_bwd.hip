@@ -485,7 +485,7 @@ hipError_t launch_bwd_pre(Elem e, int d, const BwdArgs &a, hipStream_t stream) {
 
 hipError_t launch_bwd_dkdv(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                            hipStream_t stream) {
-    if (e != Elem::F32 && (d == 64 || d == 128)) return launch_bwd_dkdv16(e, d, causal, dropout, a, stream);
+    if (e != Elem::F32 && (d == 64 || d == 128 || d == 256)) return launch_bwd_dkdv16(e, d, causal, dropout, a, stream);
     FA_DISPATCH_ELEM_D(e, d, launch_dkdv_t, causal, dropout, a, stream)
 }
 

@@ -22,10 +22,11 @@
 
 namespace fa {
 
-// One workgroup owns 128 keys: two pairs of wavefronts, each pair 64 keys.
-// The four products of the backward are split between the two wavefronts
-// of a pair, so that each holds only one 128x64 accumulator (dV^T or dK^T,
-// keys along the lanes) besides its operands:
+// One workgroup owns 128 keys (64 at d = 256): two pairs of wavefronts,
+// each pair 64 keys (32).  The four products of the backward are split
+// between the two wavefronts of a pair, so that each holds only one d x 64
+// (d x 32) accumulator (dV^T or dK^T, keys along the lanes) besides its
+// operands:
 //   A: S = Q K^T (K of its keys in AGPRs), P = exp(S - LSE) and the keep
 //      bits, then dV^T += dO^T (keep P);
 //   B: dP = dO V^T (V in AGPRs), dS = P o (dP keep c - D) with P taken from
@@ -52,7 +53,10 @@ namespace fa {
 template <typename T, int D>
 struct Dkdv16Tile {
     static constexpr int NW = 4;                       // 2 pairs x (A, B)
-    static constexpr int KP = 64;                      // keys per pair
+    // 32-key blocks per pair: two, one at d = 256 (where a d x 64 fp32
+    // accumulator and the 64 keys' operands would not fit the registers)
+    static constexpr int NKP = D == 256 ? 1 : 2;
+    static constexpr int KP = 32 * NKP;                // keys per pair
     static constexpr int BK = 2 * KP;                  // keys per workgroup
     static constexpr int BQ = 32;                      // query rows per step
     static constexpr int THREADS = NW * kWave;
@@ -72,7 +76,7 @@ template <typename T, int D, bool CAUSAL, bool DROPOUT>
 __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     using TL = Dkdv16Tile<T, D>;
     using SW = Swz<D>;
-    constexpr int NW = TL::NW, KP = TL::KP, BK = TL::BK, BQ = TL::BQ;
+    constexpr int NW = TL::NW, NKP = TL::NKP, KP = TL::KP, BK = TL::BK, BQ = TL::BQ;
     constexpr int TB = TL::TB, LOADS = TL::LOADS;
     constexpr int RB = SW::ROW_BYTES;
     constexpr int NDC = D / 16;
@@ -83,11 +87,11 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     __shared__ __attribute__((aligned(1024))) char qs0[TB], qs1[TB], qs2[TB], qs3[TB], os0[TB], os1[TB];
     __shared__ __attribute__((aligned(256))) float nl_s[2][64];
     __shared__ __attribute__((aligned(256))) float dv_s[4][64];
-    __shared__ __attribute__((aligned(1024))) float pex[2][2][32 * 64];   // [slot][pair][regs x lanes]
+    __shared__ __attribute__((aligned(1024))) float pex[2][2][16 * NKP * 64];   // [slot][pair][regs x lanes]
     // Dropout keep masks: 16-bit 0x0000 / 0xFFFF per (row, key) of a pair's
-    // 32 x 64 block, row-major with a 192-byte row pitch (conflict-free for
-    // the transposed reads); four tiles in flight.
-    constexpr int MP = 192;
+    // 32 x KP block, row-major with a row pitch of 2 KP + 64 bytes (192 at
+    // KP = 64: conflict-free for the transposed reads); four tiles in flight.
+    constexpr int MP = 2 * KP + 64;
     __shared__ __attribute__((aligned(1024))) char mk[DROPOUT ? 4 : 1][2][32 * MP];
     auto qbuf = [&](int s) {
         return s == 0 ? (lds_char *)qs0 : s == 1 ? (lds_char *)qs1 : s == 2 ? (lds_char *)qs2 : (lds_char *)qs3;
@@ -120,11 +124,11 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     const int NTQ = (N + BQ - 1) / BQ - j0;   // query tiles streamed
 
     // ---- the pair's K (A) or V (B) rows: B operands, one key per lane, in AGPRs.
-    frag_t<T> kv[2][NDC];
+    frag_t<T> kv[NKP][NDC];
     {
         const T *src = role == 0 ? Kg : Vg;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKP; ++kb) {
             int key = kp0 + 32 * kb + lq;
             key = key < Nk ? key : Nk - 1;
 #pragma unroll
@@ -150,18 +154,31 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     // ---- loads: Q and dO tiles (all four wavefronts, LOADS instructions
     // each), -LSE log2(e) rows (the A wavefronts) and D/c rows (the B
     // wavefronts).
+    // Load instruction i of a wavefront fills tile rows R0 + i RSTEP.  The
+    // swizzle repeats every 16 rows: where RSTEP is a multiple of 16 every
+    // instruction uses the lane offset of R0 (the row step goes into the
+    // scalar offset); otherwise (d = 256) each has its own.
     constexpr int RSTEP = NW * kWave / SW::CPR;
+    constexpr bool ONE_OFF = RSTEP % 16 == 0;
     const int R0 = (wave * kWave + lane) / SW::CPR;
-    const uint32_t gcol = (uint32_t)(((lane % SW::CPR) ^ (int)SW::f(R0)) * 8);
-    const uint32_t lane_boff = ((uint32_t)R0 * D + gcol) * 2;
+    uint32_t lane_boff[ONE_OFF ? 1 : LOADS];
+#pragma unroll
+    for (int i = 0; i < (ONE_OFF ? 1 : LOADS); ++i) {
+        const uint32_t r = (uint32_t)(R0 + i * RSTEP);
+        lane_boff[i] = (r * D + (((uint32_t)lane % SW::CPR) ^ SW::f(r)) * 8) * 2;
+    }
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, head_bytes), ors = make_rsrc(dOg, head_bytes);
     const __amdgpu_buffer_rsrc_t rrs =
         role == 0 ? make_rsrc(a.nl2 + (size_t)bh * (size_t)N, (uint32_t)N * 4)
                   : make_rsrc(a.dvec + (size_t)bh * (size_t)N, (uint32_t)N * 4);
     auto load_tile_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
-        buf2lds16(rs, lane_boff, (uint32_t)((j0 + t) * BQ + i * RSTEP) * (uint32_t)(D * 2),
-                  buf + (wave + i * NW) * (kWave * 16));
+        if constexpr (ONE_OFF)
+            buf2lds16(rs, lane_boff[0], (uint32_t)((j0 + t) * BQ + i * RSTEP) * (uint32_t)(D * 2),
+                      buf + (wave + i * NW) * (kWave * 16));
+        else
+            buf2lds16(rs, lane_boff[i], (uint32_t)((j0 + t) * BQ) * (uint32_t)(D * 2),
+                      buf + (wave + i * NW) * (kWave * 16));
     };
     auto load_rows = [&](int t, lds_char *buf) {   // 64 fp32 rows from the tile's first row
         buf2lds4(rrs, (uint32_t)lane * 4, (uint32_t)((j0 + t) * BQ) * 4, buf);
@@ -178,19 +195,21 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     };
 
     const float sl2 = a.scale_log2, dc = a.drop_c;
-    f32x16 acc[NDB][2];          // dV^T (A) or dK^T (B): [d block][key block]
+    f32x16 acc[NDB][NKP];        // dV^T (A) or dK^T (B): [d block][key block]
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) { acc[db][0] = f32x16{}; acc[db][1] = f32x16{}; }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int kb = 0; kb < NKP; ++kb) acc[db][kb] = f32x16{};
 
     // Masking of tile t for this pair: key > query (causal), key >= N, row >= N.
     auto is_edge = [&](int t) {
         const int qt0 = (j0 + t) * BQ;
         return (qt0 + BQ > N) || (kp0 + KP > Nk) || (CAUSAL && kp0 + KP - 1 > qt0 + off);
     };
-    auto apply_mask = [&](f32x16 (&s)[2], int t) {
+    auto apply_mask = [&](f32x16 (&s)[NKP], int t) {
         const int qt0 = (j0 + t) * BQ;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKP; ++kb) {
             const int key = kp0 + 32 * kb + lq;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -200,17 +219,18 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         }
     };
 
-    // Keep masks of this pair's tile t: its 32 rows x 64 keys are eight
+    // Keep masks of this pair's tile t: its 32 rows x KP keys are 4 NKP
     // Philox blocks of 8 keys per row (block j: keys 8j .. 8j+7), drawn by
     // the four lanes of a row -- A lane (row lq, half g) block g, B lane
-    // (row lq, half g) blocks 2 + 3g .. 4 + 3g -- and stored as 16-bit masks.
+    // (row lq, half g) the NBB blocks from 2 + NBB g -- and stored as 16-bit
+    // masks.
     // The draw is staged (counters, then the block-rounds in order, then the
     // masks): the rounds of tile s+2 are spread over the second product
     // phase of step s and its masks are formed and stored during the first
     // phase of step s+1, so no part of the draw waits at the end of a step.
-    constexpr int NBA = 1, NBB = 3;   // blocks per lane: A, B
+    constexpr int NBA = 1, NBB = 4 * NKP / 2 - 1;   // blocks per lane: A, B
     struct MaskDraw { Philox4 c[NBB]; };
-    const int jb0 = role == 0 ? g : 2 + 3 * g;    // first block of this lane
+    const int jb0 = role == 0 ? g : 2 + NBB * g;  // first block of this lane
     auto mask_begin = [&](MaskDraw &m, int t) {
         const uint32_t grp = (uint32_t)(kp0 >> 3) + (uint32_t)jb0;
         const uint32_t row = (uint32_t)((j0 + t) * BQ + lq);
@@ -279,7 +299,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     else load_rows(0, (lds_char *)dv_s[0]);
     // K or V into AGPRs once all loads are in flight (a pin waits for its load).
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKP; ++kb)
 #pragma unroll
         for (int c = 0; c < NDC; ++c) pin_agpr(kv[kb][c]);
     if (DROPOUT) {
@@ -308,8 +328,8 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         // ============================== A: S, P, dV ==============================
         // Step s: S of tile s+1 (Q slot (s+1)%4) on the matrix cores while
         // the VALU exponentiates tile s; then dV of tile s (dO slot s%2).
-        f32x16 sA[2], sB[2];
-        auto a_step = [&](auto r_c, f32x16 (&sc)[2], f32x16 (&sn)[2], int s) {
+        f32x16 sA[NKP], sB[NKP];
+        auto a_step = [&](auto r_c, f32x16 (&sc)[NKP], f32x16 (&sn)[NKP], int s) {
             constexpr int R = decltype(r_c)::value;
             lds_char *qb = qbuf((R + 1) & 3);
             lds_char *ob = obuf(R & 1);
@@ -323,15 +343,15 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             f32x4 l4[4];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) l4[q4] = *(const FA_LDS f32x4 *)(nlp + 8 * q4 + 4 * g);
-            u32x2 mw[2][4];
+            u32x2 mw[NKP][4];
             if (DROPOUT) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKP; ++kb)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) mw[kb][q4] = read_masks(R, kb, q4);
             }
-            float pv[2][4][4];
-            uint32_t pp[2][8];
+            float pv[NKP][4][4];
+            uint32_t pp[NKP][8];
             // P of register group (kb, q4) of tile s, also handed to B in fp32.
             auto pgroup = [&](int kb, int q4) {
                 f32x4 xo;
@@ -343,10 +363,10 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 }
                 *(FA_LDS f32x4 *)(px + ((4 * kb + q4) * kWave + lane) * 4) = xo;
             };
-            // Rounded (and kept) P of rows 8 q4 + .. for both key blocks.
+            // Rounded (and kept) P of rows 8 q4 + .. for every key block.
             auto ppair = [&](int q4) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NKP; ++kb) {
                     pp[kb][2 * q4] = pack2<T>(pv[kb][q4][0], pv[kb][q4][1]);
                     pp[kb][2 * q4 + 1] = pack2<T>(pv[kb][q4][2], pv[kb][q4][3]);
                     if (DROPOUT) {
@@ -365,24 +385,29 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             };
 
             // ---- phase 1: S of tile s+1 | P of tile s.
-            sn[0] = f32x16{};
-            sn[1] = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < NKP; ++kb) sn[kb] = f32x16{};
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
                 if (c + 2 < NDC) qf[(c + 2) % 3] = lds_frag<T>(qb + roff[c + 2]);
                 if (c == NDC - 2) of[0] = ofrag(0);
                 if (c == NDC - 1) of[1] = ofrag(1);
                 mma(sn[0], qf[c % 3], kv[0][c]);
-                if (NDC == 8) {
-                    if (c < 6) pgroup(c & 1, c >> 1);     // q4 = 0, 1, 2
-                    else ppair(c - 6);                    // pairs of q4 = 0, 1
+                if constexpr (NKP == 2) {
+                    if (NDC == 8) {
+                        if (c < 6) pgroup(c & 1, c >> 1);     // q4 = 0, 1, 2
+                        else ppair(c - 6);                    // pairs of q4 = 0, 1
+                    } else {
+                        pgroup(0, c);
+                        pgroup(1, c);
+                        ppair(c);
+                    }
                 } else {
-                    pgroup(0, c);
-                    pgroup(1, c);
-                    ppair(c);
+                    if (c < 4) pgroup(0, c);
+                    else if (c < 8) ppair(c - 4);
                 }
                 if (DROPOUT && c == 1) mask_end_blk(pend, R + 1, 0);
-                mma(sn[1], qf[c % 3], kv[1][c]);
+                if constexpr (NKP == 2) mma(sn[1], qf[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- phase 2: dV^T += dO^T (keep P) of tile s | keep masks of
@@ -398,17 +423,19 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                 const int cc = j / NDB, db = j % NDB;
                 if (j + 2 < 2 * NDB) of[(j + 2) % 3] = ofrag(j + 2);
                 if (DROPOUT) {
-                    if (NDB == 4) mask_rounds(CNA{}, md, UA[j], UA[j + 1]);
-                    else mask_rounds(CNA{}, md, UA64[j], UA64[j + 1]);
+                    if constexpr (NDB == 4) mask_rounds(CNA{}, md, UA[j], UA[j + 1]);
+                    else if constexpr (NDB == 2) mask_rounds(CNA{}, md, UA64[j], UA64[j + 1]);
+                    else   // d = 256 (P finished in phase 1): spread evenly
+                        mask_rounds(CNA{}, md, (10 * NBA * j) / (2 * NDB), (10 * NBA * (j + 1)) / (2 * NDB));
                 }
-                if (NDC == 8) {
+                if constexpr (NKP == 2 && NDC == 8) {
                     if (j == 0) pgroup(0, 3);
                     if (j == 1) pgroup(1, 3);
                     if (j == 2) ppair(2);
                     if (j == 3) ppair(3);
                 }
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NKP; ++kb) {
                     u32x4 p4;
                     p4[0] = pp[kb][4 * cc + 0];
                     p4[1] = pp[kb][4 * cc + 1];
@@ -426,13 +453,13 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
 
         // prologue: S of tile 0 (Q slot 0).
         if (NTQ > 0) {
-            sA[0] = f32x16{};
-            sA[1] = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < NKP; ++kb) sA[kb] = f32x16{};
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
                 const frag_t<T> qfr = lds_frag<T>(qbuf(0) + roff[c]);
-                mma(sA[0], qfr, kv[0][c]);
-                mma(sA[1], qfr, kv[1][c]);
+#pragma unroll
+                for (int kb = 0; kb < NKP; ++kb) mma(sA[kb], qfr, kv[kb][c]);
             }
             if (is_edge(0)) apply_mask(sA, 0);
         }
@@ -451,9 +478,13 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         // Step s: dP of tile s (dO slot s%2) on the matrix cores while the
         // VALU forms dS of tile s-1 from its dP, A's P (P slot (s-1)%2) and D
         // (D slot (s-1)%4); then dK of tile s-1 (Q slot (s-1)%4).
-        f32x16 dA[2], dB[2];
-        constexpr int IPG = 8 / NDC;     // dS register groups per product group
-        auto b_step = [&](auto r_c, auto hp_c, f32x16 (&dcur)[2], f32x16 (&dprv)[2], int s) {
+        f32x16 dA[NKP], dB[NKP];
+        // dS register groups ("items") i = (key block i % NKP, rows q4 = i / NKP);
+        // item i is formed in phase-1 group ig(i), its P and masks fetched
+        // two groups earlier.
+        constexpr int NI = 4 * NKP;
+        auto ig = [](int i) { return (i * NDC) / NI; };
+        auto b_step = [&](auto r_c, auto hp_c, f32x16 (&dcur)[NKP], f32x16 (&dprv)[NKP], int s) {
             constexpr int R = decltype(r_c)::value;
             constexpr bool HP = decltype(hp_c)::value;
             lds_char *ob = obuf(R & 1);
@@ -465,22 +496,22 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             frag_t<T> of[3], qt[3];
             of[0] = lds_frag<T>(ob + roff[0]);
             of[1] = lds_frag<T>(ob + roff[1]);
-            f32x4 d4[4], x4[8];
-            u32x2 mw[8];
-            // item i = register group (kb, q4) = (i & 1, i >> 1)
+            f32x4 d4[4], x4[NI];
+            u32x2 mw[NI];
             auto fetch = [&](int i) {
-                x4[i] = *(const FA_LDS f32x4 *)(px + ((4 * (i & 1) + (i >> 1)) * kWave + lane) * 4);
-                if (DROPOUT) mw[i] = read_masks(R + 3, i & 1, i >> 1);
+                x4[i] = *(const FA_LDS f32x4 *)(px + ((4 * (i % NKP) + i / NKP) * kWave + lane) * 4);
+                if (DROPOUT) mw[i] = read_masks(R + 3, i % NKP, i / NKP);
             };
             if (HP) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) d4[q4] = *(const FA_LDS f32x4 *)(dvp + 8 * q4 + 4 * g);
 #pragma unroll
-                for (int i = 0; i < 2 * IPG; ++i) fetch(i);
+                for (int i = 0; i < NI; ++i)
+                    if (ig(i) < 2) fetch(i);
             }
-            uint32_t sp[2][8];
+            uint32_t sp[NKP][8];
             auto dsitem = [&](int i) {
-                const int kb = i & 1, q4 = i >> 1;
+                const int kb = i % NKP, q4 = i / NKP;
                 const f32x4 x = x4[i];
                 float ds[4];
 #pragma unroll
@@ -508,35 +539,36 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
             };
 
             // ---- phase 1: dP of tile s | dS of tile s-1.
-            dcur[0] = f32x16{};
-            dcur[1] = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < NKP; ++kb) dcur[kb] = f32x16{};
 #pragma unroll
             for (int c = 0; c < NDC; ++c) {
                 if (c + 2 < NDC) of[(c + 2) % 3] = lds_frag<T>(ob + roff[c + 2]);
                 if (HP) {
 #pragma unroll
-                    for (int i = IPG * (c + 2); i < IPG * (c + 3); ++i)
-                        if (i < 8) fetch(i);
+                    for (int i = 0; i < NI; ++i)
+                        if (ig(i) == c + 2) fetch(i);
                     if (c == NDC - 2) qt[0] = qfrag(0);
                     if (c == NDC - 1) qt[1] = qfrag(1);
                 }
                 mma(dcur[0], of[c % 3], kv[0][c]);
                 if (HP) {
 #pragma unroll
-                    for (int i = IPG * c; i < IPG * (c + 1); ++i) dsitem(i);
+                    for (int i = 0; i < NI; ++i)
+                        if (ig(i) == c) dsitem(i);
                 }
-                // masks of the pending draw: blocks 0, 1, 2 after products
-                // c = 1, 3, 5 (d = 128) or 1, 2, 3 (d = 64)
-                if (DROPOUT && (NDC == 8 ? (c & 1) && c < 6 : c >= 1))
-                    mask_end_blk(pend, R + 1, NDC == 8 ? c >> 1 : c - 1);
-                mma(dcur[1], of[c % 3], kv[1][c]);
+                // masks of the pending draw: block h after product c = 2h + 1
+                // (d >= 128) or h + 1 (d = 64)
+                if (DROPOUT && (NDC >= 8 ? (c & 1) && (c >> 1) < NBB : c >= 1 && c - 1 < NBB))
+                    mask_end_blk(pend, R + 1, NDC >= 8 ? c >> 1 : c - 1);
+                if constexpr (NKP == 2) mma(dcur[1], of[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // ---- phase 2: dK^T += Q^T dS of tile s-1 | keep masks of tile
             // s+2 (block-rounds, cumulative count before group j: UB[j]).
             constexpr int UB[9] = {0, 4, 8, 12, 16, 19, 22, 26, 30};
             constexpr int UB64[5] = {0, 8, 15, 23, 30};
-            static_assert(UB[8] == 10 * NBB && UB64[4] == 10 * NBB, "B draws NBB blocks");
+            static_assert(NKP == 1 || (UB[8] == 10 * NBB && UB64[4] == 10 * NBB), "B draws NBB blocks");
             MaskDraw md;
             if (DROPOUT) mask_begin(md, s + 2);
             if (HP) {
@@ -545,11 +577,13 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     const int cc = j / NDB, db = j % NDB;
                     if (j + 2 < 2 * NDB) qt[(j + 2) % 3] = qfrag(j + 2);
                     if (DROPOUT) {
-                        if (NDB == 4) mask_rounds(CNB{}, md, UB[j], UB[j + 1]);
-                        else mask_rounds(CNB{}, md, UB64[j], UB64[j + 1]);
+                        if constexpr (NDB == 4) mask_rounds(CNB{}, md, UB[j], UB[j + 1]);
+                        else if constexpr (NDB == 2) mask_rounds(CNB{}, md, UB64[j], UB64[j + 1]);
+                        else   // d = 256: spread evenly
+                            mask_rounds(CNB{}, md, (10 * NBB * j) / (2 * NDB), (10 * NBB * (j + 1)) / (2 * NDB));
                     }
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
+                    for (int kb = 0; kb < NKP; ++kb) {
                         u32x4 p4;
                         p4[0] = sp[kb][4 * cc + 0];
                         p4[1] = sp[kb][4 * cc + 1];
@@ -587,7 +621,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     const float osc = DROPOUT ? (role == 0 ? dc : a.scale * dc) : (role == 0 ? 1.f : a.scale);
     void *dst = role == 0 ? a.dv : a.dk;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKP; ++kb) {
         const int key = kp0 + 32 * kb + lq;
         if (key < Nk) {
 #pragma unroll
@@ -630,10 +664,12 @@ hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const Bwd
     switch (e) {
     case Elem::BF16:
         return d == 64 ? launch_dkdv16_t<bf16, 64>(causal, dropout, a, stream)
-                       : launch_dkdv16_t<bf16, 128>(causal, dropout, a, stream);
+               : d == 128 ? launch_dkdv16_t<bf16, 128>(causal, dropout, a, stream)
+                          : launch_dkdv16_t<bf16, 256>(causal, dropout, a, stream);
     case Elem::F16:
         return d == 64 ? launch_dkdv16_t<f16, 64>(causal, dropout, a, stream)
-                       : launch_dkdv16_t<f16, 128>(causal, dropout, a, stream);
+               : d == 128 ? launch_dkdv16_t<f16, 128>(causal, dropout, a, stream)
+                          : launch_dkdv16_t<f16, 256>(causal, dropout, a, stream);
     default:
         return hipErrorInvalidValue;
     }
