@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_pp.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_bwd16.hip",
-           "fa_dkdv16.hip", "fa_noalloc.hip"]
+           "fa_dq256.hip", "fa_dkdv16.hip", "fa_noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
@@ -27,13 +27,16 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 
 # Kernel sources: the inputs are finite by contract (infinities are still
 # honoured, they carry the masks), so NaN-preserving canonicalisation of
-# max() is not needed.  The forward and dQ kernels select matrix-core
-# results into VGPRs so that the softmax reads scores without AGPR copies;
-# the dK/dV kernel keeps them in AGPRs (its accumulators need the room).
+# max() is not needed.  The generic forward, the dK/dV kernel and the dQ
+# kernel at d = 64 and 128 select matrix-core results into VGPRs, so that
+# the softmax and dS arithmetic reads them without AGPR copies; the
+# direct-load forward, the FP8 forward and the d = 256 dQ kernel leave them
+# in AGPRs, which hold their output accumulators.
 KERNEL_FLAGS = ["-fno-honor-nans"]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 PER_SOURCE = {"fa_fwd.hip": KERNEL_FLAGS + VGPR_FORM, "fa_fwd_pp.hip": KERNEL_FLAGS,
               "fa_fwd_fp8.hip": KERNEL_FLAGS, "fa_bwd16.hip": KERNEL_FLAGS + VGPR_FORM,
+              "fa_dq256.hip": KERNEL_FLAGS,
               "fa_dkdv16.hip": KERNEL_FLAGS + VGPR_FORM}
 
 

@@ -91,12 +91,14 @@ hipError_t launch_bwd_dkdv(Elem e, int d, bool causal, bool dropout, const BwdAr
                            hipStream_t stream);
 hipError_t launch_bwd_dq(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                          hipStream_t stream);
-// 16-bit inputs only (bf16, f16).
+// 16-bit inputs only (bf16, f16); d = 64, 128, 256.
 hipError_t launch_bwd_dq16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                            hipStream_t stream);
+hipError_t launch_bwd_dq16_256(Elem e, bool causal, bool dropout, const BwdArgs &a, hipStream_t stream);
 hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                              hipStream_t stream);
-// 16-bit inputs at d = 128: eight wavefronts per workgroup, two per SIMD.
+// 16-bit inputs at d = 64, 128, 256: four wavefronts per workgroup, two
+// workgroups per CU (one at d = 256).
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                          hipStream_t stream);
 // e4m3 inputs at d = 128 with per-(b, h) descale factors; bf16 (or fp32) O.
