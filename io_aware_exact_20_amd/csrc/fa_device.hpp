@@ -195,6 +195,29 @@ __device__ __forceinline__ uint32_t keep_signs_from_blocks(const Philox4 &b0, co
     return own | other_half(send);
 }
 
+// Keep masks (keep_mask2 layout) of the eight probability pairs one lane
+// holds in a 32x32 accumulator with one query row per lane: pair i is
+// registers 2i, 2i+1, keys 8(i/2) + 4g + 2(i%2) + {0, 1} of the 32-key block
+// (g = lane / 32).  Lane (row, g) draws 8-key blocks 2g (b0) and 2g+1 (b1)
+// of the row; pair i takes word 2g + i%2 of block i/2.  So the lower half
+// of the wavefront needs words 0, 1 and the upper half words 2, 3 of every
+// block, and one v_permlane32_swap per (block, word) pair -- the upper half
+// of the first operand traded for the lower half of the second -- hands
+// each half the words the other half drew.
+__device__ __forceinline__ void keep_masks_from_blocks(const Philox4 &b0, const Philox4 &b1, uint32_t kc2,
+                                                       uint32_t (&m)[8]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const Philox4 &b = h ? b1 : b0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const auto r = __builtin_amdgcn_permlane32_swap(b.x[e], b.x[2 + e], false, false);
+            m[2 * h + e] = keep_mask2(r[0], kc2);       // block h: pairs 2h + e
+            m[4 + 2 * h + e] = keep_mask2(r[1], kc2);   // block 2 + h: pairs 4 + 2h + e
+        }
+    }
+}
+
 // Keep bits of the sixteen keys one lane holds in a 32x32 accumulator that
 // has one query row per lane (register r <-> key kbase + 8(r/4) + 4g +
 // r%4, g = lane / 32): bit r of the result.  Each half-wavefront draws two

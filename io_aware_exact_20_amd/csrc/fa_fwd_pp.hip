@@ -221,17 +221,16 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) apply_mask(s[kb], t, kb);
         }
-        // Keep decisions of each 32-key block, in the sign layout (drawn
-        // before the scores are read into vector registers).
-        uint32_t keep_blk[NKB];
+        // Keep masks of each 32-key block's probability pairs (drawn before
+        // the scores are read into vector registers).
+        uint32_t keep_m[NKB][8];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            keep_blk[kb] = 0;
             if (DROPOUT) {
                 const uint32_t grp = (uint32_t)((klo + t * BC + 32 * kb) >> 3) + 2 * (uint32_t)g;
                 const Philox4 b0 = philox4x32_10(grp, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
                 const Philox4 b1 = philox4x32_10(grp + 1, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
-                keep_blk[kb] = keep_signs_from_blocks(b0, b1, kc2);
+                keep_masks_from_blocks(b0, b1, kc2, keep_m[kb]);
             }
         }
         float mx = kNegInf;
@@ -261,7 +260,6 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const uint32_t keep = keep_blk[kb];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float p0 = fast_exp2(fmaf(s[kb][2 * i], sl2, -mu));
@@ -270,11 +268,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
                 if (i & 1) acc1 = (acc1 + p0) + p1;
                 else acc0 = (acc0 + p0) + p1;
                 uint32_t w = pack2<T>(p0, p1);
-                if (DROPOUT) {
-                    // decisions of pair i in the sign bits of the two halves
-                    const i16x2 sg = __builtin_bit_cast(i16x2, keep << i);
-                    w &= __builtin_bit_cast(uint32_t, sg >> (i16x2){15, 15});
-                }
+                if (DROPOUT) w &= keep_m[kb][i];
                 pp[8 * kb + i] = w;
             }
         }
