@@ -184,8 +184,10 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
             if (kk > lim) s[r] = kNegInf;
         }
     };
+    // Keep masks of a row block's eight register pairs (keep_masks_from_blocks).
+    struct KeepM { uint32_t m[8]; };
     // dS of pair i (registers 2i, 2i+1) of one row block, packed.
-    auto ds_pair = [&](const f32x16 &s, const f32x16 &dp, uint32_t keep, int nb, int i) {
+    auto ds_pair = [&](const f32x16 &s, const f32x16 &dp, const KeepM &keep, int nb, int i) {
         float ds[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -193,9 +195,10 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
             const float p = fast_exp2(fmaf(s[r], sl2, -lse2[nb]));
             float dpv = dp[r];
             if (DROPOUT) {
-                // keep decision of register r = 2i + e (bit 15 - i or 31 - i
-                // of the sign layout) sign-extended to a 32-bit mask: dP or +0.
-                const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)keep, e ? 31 - i : 15 - i, 1);
+                // the 16-bit mask of register r = 2i + e (half e of pair i)
+                // sign-extended to 32 bits: dP or +0.
+                const uint32_t m = e ? (uint32_t)((int)keep.m[i] >> 16)
+                                     : (uint32_t)__builtin_amdgcn_sbfe((int)keep.m[i], 0, 16);
                 dpv = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, dpv) & m);
             }
             ds[e] = p * (dpv - dvec[nb]);
@@ -204,11 +207,10 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         pin_vgpr(v);   // keeps the work in its group (no sinking)
         return v;
     };
-    // The keep decisions of block nb of tile t (those of keep_bits_row, in the
-    // sign layout of keep_signs_from_blocks), drawn in stages:
-    // counters, then 20 block-rounds in order (unit u: round u/2 of block
-    // u%2), then the bits, so that the rounds can sit between the dQ
-    // products, which have no other VALU work.
+    // The keep decisions of block nb of tile t, drawn in stages: counters,
+    // then 20 block-rounds in order (unit u: round u/2 of block u%2), then
+    // the masks, so that the rounds can sit between the dQ products, which
+    // have no other VALU work.
     struct KeepDraw { Philox4 c[2]; };
     auto keep_begin = [&](KeepDraw &k, int t, int nb) {
         const uint32_t grp = (uint32_t)((t * BC) >> 3) + 2 * (uint32_t)g;
@@ -231,19 +233,25 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         }
     };
     const uint32_t kc2 = keep_cmp_const(a.drop_T);
-    auto keep_end = [&](KeepDraw &k) { return keep_signs_from_blocks(k.c[0], k.c[1], kc2); };
+    auto keep_end = [&](KeepDraw &k) {
+        KeepM km;
+        keep_masks_from_blocks(k.c[0], k.c[1], kc2, km.m);
+        return km;
+    };
 
     // Scores of the lane's blocks: `cur` = the block being produced, `prv`
     // = the block whose dS is being formed.
     f32x16 s_a, dp_a, s_b, dp_b;
     uint32_t dsa[8], dsb[8];
-    uint32_t keep_a = 0xFFFFu, keep_b = 0xFFFFu;
+    KeepM keep_a, keep_b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) keep_a.m[i] = keep_b.m[i] = 0xFFFFFFFFu;
 
     // 1x: S and dP of block nb of tile t (slot sl), interleaved with the dS
     // pairs of another block (sp/dpp, results into dso); loads of tile
     // t + 1 are spread over the groups.
     auto phase1 = [&](auto nb_c, auto sl_c, auto ds_c, auto ld_c, f32x16 &s, f32x16 &dp,
-                      const f32x16 &sp, const f32x16 &dpp, uint32_t keep_p, int nbp, uint32_t (&dso)[8],
+                      const f32x16 &sp, const f32x16 &dpp, const KeepM &keep_p, int nbp, uint32_t (&dso)[8],
                       int t, auto sln_c) {
         constexpr int NB_ = decltype(nb_c)::value, SL = decltype(sl_c)::value, SLN = decltype(sln_c)::value;
         constexpr bool do_ds = decltype(ds_c)::value, do_load = decltype(ld_c)::value;
@@ -389,7 +397,7 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         // (inlined by force: as calls, the arrays they touch would live in
         // scratch memory)
         auto step1p = [&](auto hp_c, auto sl_c, auto sp_c, auto sn_c, f32x16 &s_c, f32x16 &dp_c,
-                          const f32x16 &s_p, const f32x16 &dp_p, uint32_t keep_p, uint32_t &keep_c,
+                          const f32x16 &s_p, const f32x16 &dp_p, const KeepM &keep_p, KeepM &keep_c,
                           int tt) __attribute__((always_inline)) {
             constexpr bool HP = decltype(hp_c)::value;
             // 1: tile tt | dS of tile tt-1 | loads of tile tt+1.
