@@ -172,29 +172,6 @@ __device__ __forceinline__ uint32_t keep_mask2(uint32_t w, uint32_t kc2) {
     return __builtin_bit_cast(uint32_t, d >> (i16x2){15, 15});
 }
 
-// The keep decisions of keep_bits_row in the layout the 16-bit forward
-// masks its rounded probability pairs with: pair i (registers 2i, 2i+1 of
-// the row's 16 keys) has its two decisions in bits 15 - i and 31 - i, so
-// (w << i) has them in the sign bits of its two 16-bit halves.  Word q of
-// the lane's block h (keys 2q, 2q+1 of 8-key block 2g + h of the tile) holds
-// pair 4g + 2h + (q & 1) of the lane in half q >> 1 (its own half or the
-// other one); the packed compares of keep_mask2 give the decisions as sign
-// bits, which are shifted into place and the other half's share exchanged.
-__device__ __forceinline__ uint32_t keep_signs_from_blocks(const Philox4 &b0, const Philox4 &b1,
-                                                           uint32_t kc2) {
-    const uint32_t g = lane_in_wave() >> 5;
-    auto sgn = [&](uint32_t w) {   // 0x80008000 where a lane of w is kept
-        const i16x2 lane = __builtin_bit_cast(i16x2, w ^ 0x80008000u);
-        return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(i16x2, kc2), lane)) &
-               0x80008000u;
-    };
-    // halves 0 (words 0, 1) and 1 (words 2, 3), pairs 2h + (q & 1) before the 4g offset
-    const uint32_t to0 = sgn(b0.x[0]) | (sgn(b0.x[1]) >> 1) | (sgn(b1.x[0]) >> 2) | (sgn(b1.x[1]) >> 3);
-    const uint32_t to1 = sgn(b0.x[2]) | (sgn(b0.x[3]) >> 1) | (sgn(b1.x[2]) >> 2) | (sgn(b1.x[3]) >> 3);
-    const uint32_t own = (g ? to1 : to0) >> (4 * g), send = (g ? to0 : to1) >> (4 * g);
-    return own | other_half(send);
-}
-
 // Keep masks (keep_mask2 layout) of the eight probability pairs one lane
 // holds in a 32x32 accumulator with one query row per lane: pair i is
 // registers 2i, 2i+1, keys 8(i/2) + 4g + 2(i%2) + {0, 1} of the 32-key block
