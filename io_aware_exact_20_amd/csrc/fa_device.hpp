@@ -346,7 +346,11 @@ struct TileCopy {
 // chunk of 16 consecutive rows (matrix-core operands taken along a row), and
 // 32 lanes reading 64 contiguous bytes of 4 consecutive rows (transposed
 // reads).  An unpadded pitch also lets whole rows be filled by direct
-// global-to-LDS loads, which write 16 bytes per lane contiguously.
+// global-to-LDS loads, which write 16 bytes per lane contiguously.  At
+// d = 96 (12 chunks, a 192-byte pitch whose bank offset repeats every four
+// rows) f is the row's bits 2-3, which keeps every permutation inside an
+// aligned group of four chunks and gives the four rows of each bank class
+// distinct groups; the transposed reads then need no permutation at all.
 #define FA_LDS __attribute__((address_space(3)))
 
 template <int D>
@@ -354,8 +358,9 @@ struct Swz {
     static constexpr int CPR = D / 8;            // 16-byte chunks per row
     static constexpr int ROW_BYTES = D * 2;
     __device__ static constexpr uint32_t f(uint32_t r) {
-        return D == 128 ? (((r & 3u) << 2) | ((r >> 2) & 3u))
-                        : ((((r >> 1) & 1u) << 2) | ((r >> 2) & 3u));
+        return D == 128  ? (((r & 3u) << 2) | ((r >> 2) & 3u))
+               : D == 96 ? ((r >> 2) & 3u)
+                         : ((((r >> 1) & 1u) << 2) | ((r >> 2) & 3u));
     }
     // Byte offset of element column `col` (a multiple of 4) of row r.
     __device__ static constexpr uint32_t off(uint32_t r, uint32_t col) {

@@ -61,7 +61,8 @@ struct Dkdv16Tile {
     static constexpr int BQ = 32;                      // query rows per step
     static constexpr int THREADS = NW * kWave;
     static constexpr int TB = BQ * D * 2;              // bytes of a Q or dO tile
-    static constexpr int LOADS = TB / (kWave * 16) / NW;
+    static constexpr int CHUNKS = TB / (kWave * 16);        // 1 KB load instructions per tile
+    static constexpr int LOADS = (CHUNKS + NW - 1) / NW;    // per wavefront (d = 96: 2 or 1)
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -77,7 +78,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     using TL = Dkdv16Tile<T, D>;
     using SW = Swz<D>;
     constexpr int NW = TL::NW, NKP = TL::NKP, KP = TL::KP, BK = TL::BK, BQ = TL::BQ;
-    constexpr int TB = TL::TB, LOADS = TL::LOADS;
+    constexpr int TB = TL::TB, LOADS = TL::LOADS, CHUNKS = TL::CHUNKS;
     constexpr int RB = SW::ROW_BYTES;
     constexpr int NDC = D / 16;
     constexpr int NDB = D / 32;
@@ -154,18 +155,27 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     // ---- loads: Q and dO tiles (all four wavefronts, LOADS instructions
     // each), -LSE log2(e) rows (the A wavefronts) and D/c rows (the B
     // wavefronts).
-    // Load instruction i of a wavefront fills tile rows R0 + i RSTEP.  The
-    // swizzle repeats every 16 rows: where RSTEP is a multiple of 16 every
-    // instruction uses the lane offset of R0 (the row step goes into the
-    // scalar offset); otherwise (d = 256) each has its own.
-    constexpr int RSTEP = NW * kWave / SW::CPR;
-    constexpr bool ONE_OFF = RSTEP % 16 == 0;
-    const int R0 = (wave * kWave + lane) / SW::CPR;
+    // Load instruction i of a wavefront is the tile's 1 KB chunk c = wave +
+    // i NW, lane l filling 16-byte position p = 64 c + l (row p / CPR).
+    // Where chunks hold whole rows, instruction i fills rows R0 + i RSTEP;
+    // the swizzle repeats every 16 rows, so where RSTEP is a multiple of 16
+    // every instruction uses the lane offset of R0 (the row step goes into
+    // the scalar offset); otherwise (d = 96, 256) each has its own.  At
+    // d = 96 a tile is six chunks: waves 0 and 1 issue two, waves 2 and 3 one.
+    constexpr bool ALIGNED = kWave % SW::CPR == 0;
+    constexpr int RSTEP = ALIGNED ? NW * kWave / SW::CPR : 0;
+    constexpr bool ONE_OFF = ALIGNED && RSTEP % 16 == 0;
     uint32_t lane_boff[ONE_OFF ? 1 : LOADS];
 #pragma unroll
     for (int i = 0; i < (ONE_OFF ? 1 : LOADS); ++i) {
-        const uint32_t r = (uint32_t)(R0 + i * RSTEP);
-        lane_boff[i] = (r * D + (((uint32_t)lane % SW::CPR) ^ SW::f(r)) * 8) * 2;
+        if constexpr (ALIGNED) {
+            const uint32_t r = (uint32_t)((wave * kWave + lane) / SW::CPR + i * RSTEP);
+            lane_boff[i] = (r * D + (((uint32_t)lane % SW::CPR) ^ SW::f(r)) * 8) * 2;
+        } else {
+            const uint32_t pos = (uint32_t)((wave + i * NW) * kWave + lane);
+            const uint32_t r = pos / SW::CPR;
+            lane_boff[i] = (r * D + ((pos % SW::CPR) ^ SW::f(r)) * 8) * 2;
+        }
     }
     const uint32_t head_bytes = (uint32_t)N * D * 2;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Qg, head_bytes), ors = make_rsrc(dOg, head_bytes);
@@ -173,6 +183,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         role == 0 ? make_rsrc(a.nl2 + (size_t)bh * (size_t)N, (uint32_t)N * 4)
                   : make_rsrc(a.dvec + (size_t)bh * (size_t)N, (uint32_t)N * 4);
     auto load_tile_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
+        if (CHUNKS % NW != 0 && wave + i * NW >= CHUNKS) return;   // (wave-uniform)
         if constexpr (ONE_OFF)
             buf2lds16(rs, lane_boff[0], (uint32_t)((j0 + t) * BQ + i * RSTEP) * (uint32_t)(D * 2),
                       buf + (wave + i * NW) * (kWave * 16));
@@ -397,7 +408,7 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     if (NDC == 8) {
                         if (c < 6) pgroup(c & 1, c >> 1);     // q4 = 0, 1, 2
                         else ppair(c - 6);                    // pairs of q4 = 0, 1
-                    } else {
+                    } else if (c < 4) {                       // d = 64, 96
                         pgroup(0, c);
                         pgroup(1, c);
                         ppair(c);
@@ -663,11 +674,13 @@ hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const Bwd
                              hipStream_t stream) {
     switch (e) {
     case Elem::BF16:
-        return d == 64 ? launch_dkdv16_t<bf16, 64>(causal, dropout, a, stream)
+        return d == 64    ? launch_dkdv16_t<bf16, 64>(causal, dropout, a, stream)
+               : d == 96  ? launch_dkdv16_t<bf16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_dkdv16_t<bf16, 128>(causal, dropout, a, stream)
                           : launch_dkdv16_t<bf16, 256>(causal, dropout, a, stream);
     case Elem::F16:
-        return d == 64 ? launch_dkdv16_t<f16, 64>(causal, dropout, a, stream)
+        return d == 64    ? launch_dkdv16_t<f16, 64>(causal, dropout, a, stream)
+               : d == 96  ? launch_dkdv16_t<f16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_dkdv16_t<f16, 128>(causal, dropout, a, stream)
                           : launch_dkdv16_t<f16, 256>(causal, dropout, a, stream);
     default:

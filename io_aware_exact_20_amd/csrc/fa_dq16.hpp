@@ -49,7 +49,8 @@ struct Dq16Tile {
     static constexpr int BC = 32;                 // keys per step
     static constexpr int THREADS = NW * kWave;
     static constexpr int TILE_BYTES = BC * D * 2;
-    static constexpr int LOADS = TILE_BYTES / (kWave * 16) / NW;   // per wave per tile
+    static constexpr int CHUNKS = TILE_BYTES / (kWave * 16);       // 1 KB load instructions per tile
+    static constexpr int LOADS = (CHUNKS + NW - 1) / NW;           // per wave per tile (d = 96: 2 or 1)
     static constexpr int RING = 3;                // LDS buffers per tensor
 };
 
@@ -58,7 +59,7 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
     using TL = Dq16Tile<T, D>;
     using SW = Swz<D>;
     constexpr int NW = TL::NW, NRB = TL::NRB, RW = TL::RW, BQ = TL::BQ, BC = TL::BC;
-    constexpr int TB = TL::TILE_BYTES, LOADS = TL::LOADS;
+    constexpr int TB = TL::TILE_BYTES, LOADS = TL::LOADS, CHUNKS = TL::CHUNKS;
     constexpr int RB = SW::ROW_BYTES;
     constexpr int NDC = D / 16;   // contraction chunks of S, dP
     constexpr int NDB = D / 32;   // 32-column blocks of dQ
@@ -129,22 +130,33 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
     }
     auto toff_at = [&](int hf, int db) { return toff[hf][db % TC] + (uint32_t)(db / TC) * 128u; };
     // ---- tile loads (bounded buffer loads straight into LDS).  Load
-    // instruction i of a wavefront fills tile rows R0 + i RSTEP; the swizzle
-    // repeats every 16 rows, so where RSTEP is a multiple of 16 one lane
-    // offset serves every instruction (the row step goes into the scalar
-    // offset), otherwise (d = 256) each has its own.
-    constexpr int RSTEP = NW * kWave / SW::CPR;
-    constexpr bool ONE_OFF = RSTEP % 16 == 0;
+    // instruction i of a wavefront is the tile's 1 KB chunk c = wave + i NW,
+    // lane l filling 16-byte position p = 64 c + l (row p / CPR).  Where
+    // chunks hold whole rows, instruction i fills rows R0 + i RSTEP; the
+    // swizzle repeats every 16 rows, so where RSTEP is a multiple of 16 one
+    // lane offset serves every instruction (the row step goes into the scalar
+    // offset), otherwise (d = 96, 256) each has its own.  At d = 96 a tile is
+    // six chunks: waves 0 and 1 issue two, waves 2 and 3 one.
+    constexpr bool ALIGNED = kWave % SW::CPR == 0;
+    constexpr int RSTEP = ALIGNED ? NW * kWave / SW::CPR : 0;
+    constexpr bool ONE_OFF = ALIGNED && RSTEP % 16 == 0;
     const int R0 = (wave * kWave + lane) / SW::CPR;
     uint32_t lane_boff[ONE_OFF ? 1 : LOADS];
 #pragma unroll
     for (int i = 0; i < (ONE_OFF ? 1 : LOADS); ++i) {
-        const uint32_t r = (uint32_t)(R0 + i * RSTEP);
-        lane_boff[i] = (r * D + (((uint32_t)lane % SW::CPR) ^ SW::f(r)) * 8) * 2;
+        if constexpr (ALIGNED) {
+            const uint32_t r = (uint32_t)(R0 + i * RSTEP);
+            lane_boff[i] = (r * D + (((uint32_t)lane % SW::CPR) ^ SW::f(r)) * 8) * 2;
+        } else {
+            const uint32_t pos = (uint32_t)((wave + i * NW) * kWave + lane);
+            const uint32_t r = pos / SW::CPR;
+            lane_boff[i] = (r * D + ((pos % SW::CPR) ^ SW::f(r)) * 8) * 2;
+        }
     }
     const uint32_t head_bytes = (uint32_t)Nk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(Kg, head_bytes), vrs = make_rsrc(Vg, head_bytes);
     auto load_part = [&](__amdgpu_buffer_rsrc_t rs, int t, lds_char *buf, int i) {
+        if (CHUNKS % NW != 0 && wave + i * NW >= CHUNKS) return;   // (wave-uniform)
         if constexpr (ONE_OFF)
             buf2lds16(rs, lane_boff[0], (uint32_t)(t * BC + i * RSTEP) * (uint32_t)(D * 2),
                       buf + (wave + i * NW) * (kWave * 16));

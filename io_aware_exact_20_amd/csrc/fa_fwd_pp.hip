@@ -1,5 +1,5 @@
-// Forward of fused exact attention for 16-bit inputs at d = 64, 128 and 256
-// on gfx950, with two wavefronts per SIMD (one at d = 256).
+// Forward of fused exact attention for 16-bit inputs at d = 64, 96, 128 and
+// 256 on gfx950, with two wavefronts per SIMD (one at d = 256).
 //
 // The method is the one of the other forward kernels: Q, K, V tiled into
 // on-chip blocks, the online-softmax recurrence (running row maximum,
@@ -55,7 +55,9 @@ struct FwdPPTile {
     // 32-key blocks per tile: two without dropout (one barrier per 64 keys);
     // one with it (two measured no faster there and need the vector phase
     // inlined by force to stay out of scratch memory).
-    static constexpr int NKB = (DROPOUT || D == 256) ? 1 : 2;
+    // (d = 96: always two, a 32-key tile being six load instructions for
+    // four wavefronts)
+    static constexpr int NKB = D == 96 ? 2 : (DROPOUT || D == 256) ? 1 : 2;
     // K and V buffers each (two workgroups share the LDS); tiles are loaded
     // one step ahead.
     static constexpr int NBUF = 2;
@@ -84,11 +86,10 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     constexpr int BQ = TL::BQ, BC = TL::BC, NW = TL::NW, NKB = TL::NKB, NBUF = TL::NBUF;
     constexpr int TB = TL::TILE_BYTES, CB = TL::CHUNK_BYTES, CHUNKS = TL::CHUNKS, LOADS = TL::LOADS;
     constexpr int RB = SW::ROW_BYTES;
-    constexpr int RPC = CB / RB;      // tile rows per load instruction
     constexpr int NDC = D / 16;       // contraction chunks of S
     constexpr int NDB = D / 32;       // 32-column blocks of O
     constexpr float kNegInf = -__builtin_huge_valf();
-    static_assert(D == 64 || D == 128 || D == 256, "tile plan for d = 64, 128 and 256");
+    static_assert(D == 64 || D == 96 || D == 128 || D == 256, "tile plan for d = 64, 96, 128 and 256");
     static_assert(2 * NDB == NDC, "one V^T product per K product");
 
     // LDS: K tile t in buffer t % 2, V tile t in buffer t % 2.
@@ -142,17 +143,24 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
                 voff[hf][db] = SW::off(8 * hf + 4 * (G >> 1) + k, 32 * db + 16 * (G & 1) + 4 * j);
     }
 
-    // Tile loads.  A tile is CHUNKS load instructions of 1 KB (RPC rows
-    // each); this wavefront issues chunks c = wave + i NW (i < LPT) of both
-    // the K and the V tile of a step.  Lane l loads the logical 16-byte
-    // chunk that the swizzle places at position l % CPR of its row.
+    // Tile loads.  A tile is CHUNKS load instructions of 1 KB; this
+    // wavefront issues chunks c = wave + i NW (i < LPT) of both the K and the
+    // V tile of a step.  Lane l of chunk c fills 16-byte position p = 64 c + l
+    // of the tile (row p / CPR, position p % CPR: rows need not align with
+    // chunks, d = 96) with the logical chunk the swizzle places there.
     constexpr int LPT = CHUNKS / NW;   // chunks per tile per wavefront
     static_assert(LPT * NW == CHUNKS && 2 * LPT == LOADS, "load split");
     uint32_t lboff[LPT];
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-        const int r = RPC * (wave + i * NW) + lane / SW::CPR;
-        lboff[i] = ((uint32_t)r * D + (uint32_t)(((lane % SW::CPR) ^ (int)SW::f((uint32_t)r)) * 8)) * 2;
+        if constexpr ((CB / 16) % SW::CPR == 0) {   // whole rows per chunk
+            const int r = CB / RB * (wave + i * NW) + lane / SW::CPR;
+            lboff[i] = ((uint32_t)r * D + (uint32_t)(((lane % SW::CPR) ^ (int)SW::f((uint32_t)r)) * 8)) * 2;
+        } else {
+            const int pos = (wave + i * NW) * (CB / 16) + lane;
+            const int r = pos / SW::CPR;
+            lboff[i] = ((uint32_t)r * D + (uint32_t)(((pos % SW::CPR) ^ (int)SW::f((uint32_t)r)) * 8)) * 2;
+        }
     }
     const uint32_t head_bytes = (uint32_t)Nk * D * 2;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(K, head_bytes), vrs = make_rsrc(V, head_bytes);
@@ -216,7 +224,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     uint32_t pp[8 * NKB];    // rounded (kept) probabilities of the tile the matrix phase multiplies
 
     // Vector phase for tile t: scores s -> probabilities pp.
-    auto vec_phase = [&](int t) {
+    auto vec_phase = [&](int t) __attribute__((always_inline)) {
         if (is_edge(t)) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) apply_mask(s[kb], t, kb);
@@ -449,13 +457,15 @@ static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, h
 
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                          hipStream_t stream) {
-    if (d != 64 && d != 128 && d != 256) return hipErrorInvalidValue;
+    if (d != 64 && d != 96 && d != 128 && d != 256) return hipErrorInvalidValue;
     if (e == Elem::BF16)
-        return d == 64 ? launch_fwd_pp_t<bf16, 64>(causal, dropout, a, stream)
+        return d == 64    ? launch_fwd_pp_t<bf16, 64>(causal, dropout, a, stream)
+               : d == 96  ? launch_fwd_pp_t<bf16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream)
                           : launch_fwd_pp_t<bf16, 256>(causal, dropout, a, stream);
     if (e == Elem::F16)
-        return d == 64 ? launch_fwd_pp_t<f16, 64>(causal, dropout, a, stream)
+        return d == 64    ? launch_fwd_pp_t<f16, 64>(causal, dropout, a, stream)
+               : d == 96  ? launch_fwd_pp_t<f16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream)
                           : launch_fwd_pp_t<f16, 256>(causal, dropout, a, stream);
     return hipErrorInvalidValue;
