@@ -369,6 +369,7 @@ struct Swz {
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef FA_LDS char lds_char;
 
 // 16-byte LDS read (the compiler folds constant parts of the address into

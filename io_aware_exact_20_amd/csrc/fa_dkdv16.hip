@@ -65,8 +65,6 @@ struct Dkdv16Tile {
     static constexpr int LOADS = (CHUNKS + NW - 1) / NW;    // per wavefront (d = 96: 2 or 1)
 };
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 // 4 bytes per lane at byte offset voff + soff straight into LDS at base + 4 l.
 __device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                          lds_char *base) {

@@ -404,7 +404,41 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     const size_t prow = ((size_t)split * (size_t)BH + (size_t)bh) * (size_t)N;
     const float l_tot = sum_halves(l_run);
     const float inv = l_tot > 0.f ? (DROPOUT ? a.drop_c : 1.f) / l_tot : 0.f;
-    if (qrow < N) {
+    if (!part && !a.out_f32) {
+        // 16-bit O through LDS: a lane's registers hold 4-column pieces of
+        // its row, so each wavefront writes its 32 rows into a tile buffer of
+        // its own (swizzled like the tiles, conflict-free) and stores them
+        // back as whole rows, 16 bytes per lane.  The barrier makes sure every
+        // direct load has landed and every tile read is done.
+        __syncthreads();
+        lds_char *ob = wave == 0 ? (lds_char *)ks0 : wave == 1 ? (lds_char *)ks1
+                     : wave == 2 ? (lds_char *)vs0 : (lds_char *)vs1;
+        static_assert(TB >= 32 * D * 2, "a tile buffer holds a wavefront's output rows");
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int col = 32 * db + 8 * rr + 4 * g;
+                u32x2 w;
+                w[0] = pack2<T>(o[db][4 * rr + 0] * inv, o[db][4 * rr + 1] * inv);
+                w[1] = pack2<T>(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
+                *(FA_LDS u32x2 *)(ob + SW::off((uint32_t)lq, (uint32_t)col)) = w;
+            }
+        T *O = reinterpret_cast<T *>(a.o) + head;
+        constexpr int NP = 32 * SW::CPR;          // 16-byte pieces of the wavefront's rows
+#pragma unroll
+        for (int i = 0; i < (NP + kWave - 1) / kWave; ++i) {
+            const int pc = i * kWave + lane;
+            const int r = pc / SW::CPR, x = pc % SW::CPR;
+            if ((NP % kWave == 0 || pc < NP) && q0w + r < N) {
+                const u32x4 v = *(const FA_LDS u32x4 *)(ob + SW::off((uint32_t)r, (uint32_t)(8 * x)));
+                *(u32x4 *)(O + (size_t)(q0w + r) * D + 8 * x) = v;
+            }
+        }
+        if (qrow < N && g == 0)
+            a.lse[(size_t)bh * (size_t)N + qrow] =
+                l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : kNegInf;
+    } else if (qrow < N) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
