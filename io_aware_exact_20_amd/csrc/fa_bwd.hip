@@ -483,32 +483,24 @@ hipError_t launch_bwd_pre(Elem e, int d, const BwdArgs &a, hipStream_t stream) {
     FA_DISPATCH_ELEM_D(e, d, launch_pre_t, a, stream)
 }
 
-// The generic dK/dV and dQ kernels serve fp32 and the 16-bit head
-// dimension 32; 16-bit d = 64, 96, 128 and 256 take the kernels of
-// fa_dkdv16.hip and fa_bwd16.hip (so no generic instance is built for them).
+// The generic dK/dV and dQ kernels serve fp32 inputs; 16-bit inputs take
+// the kernels of fa_dkdv16.hip and fa_bwd16.hip (so no generic 16-bit
+// instance is built).
 #define FA_DISPATCH_GENERIC(e, d, FN, ...)                                 \
-    switch (e) {                                                           \
-    case Elem::BF16:                                                       \
-        if (d == 32) return FN<bf16, 32>(__VA_ARGS__);                     \
-        break;                                                             \
-    case Elem::F16:                                                        \
-        if (d == 32) return FN<f16, 32>(__VA_ARGS__);                      \
-        break;                                                             \
-    case Elem::F32:                                                        \
+    if (e == Elem::F32) {                                                  \
         FA_DISPATCH_D(float, d, FN, __VA_ARGS__)                           \
-        break;                                                             \
     }                                                                      \
     return hipErrorInvalidValue;
 
 hipError_t launch_bwd_dkdv(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                            hipStream_t stream) {
-    if (e != Elem::F32 && (d == 64 || d == 96 || d == 128 || d == 256)) return launch_bwd_dkdv16(e, d, causal, dropout, a, stream);
+    if (e != Elem::F32) return launch_bwd_dkdv16(e, d, causal, dropout, a, stream);
     FA_DISPATCH_GENERIC(e, d, launch_dkdv_t, causal, dropout, a, stream)
 }
 
 hipError_t launch_bwd_dq(Elem e, int d, bool causal, bool dropout, const BwdArgs &a,
                          hipStream_t stream) {
-    if (e != Elem::F32 && (d == 64 || d == 96 || d == 128 || d == 256)) return launch_bwd_dq16(e, d, causal, dropout, a, stream);
+    if (e != Elem::F32) return launch_bwd_dq16(e, d, causal, dropout, a, stream);
     FA_DISPATCH_GENERIC(e, d, launch_dq_t, causal, dropout, a, stream)
 }
 

@@ -348,7 +348,7 @@ struct TileCopy {
 // reads).  An unpadded pitch also lets whole rows be filled by direct
 // global-to-LDS loads, which write 16 bytes per lane contiguously.  At
 // d = 96 (12 chunks, a 192-byte pitch whose bank offset repeats every four
-// rows) f is the row's bits 2-3, which keeps every permutation inside an
+// rows) and d = 32 (4 chunks, 64-byte pitch) f is the row's bits 2-3, which keeps every permutation inside an
 // aligned group of four chunks and gives the four rows of each bank class
 // distinct groups; the transposed reads then need no permutation at all.
 #define FA_LDS __attribute__((address_space(3)))
@@ -359,7 +359,7 @@ struct Swz {
     static constexpr int ROW_BYTES = D * 2;
     __device__ static constexpr uint32_t f(uint32_t r) {
         return D == 128  ? (((r & 3u) << 2) | ((r >> 2) & 3u))
-               : D == 96 ? ((r >> 2) & 3u)
+               : (D == 96 || D == 32) ? ((r >> 2) & 3u)
                          : ((((r >> 1) & 1u) << 2) | ((r >> 2) & 3u));
     }
     // Byte offset of element column `col` (a multiple of 4) of row r.

@@ -406,6 +406,13 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                     if (NDC == 8) {
                         if (c < 6) pgroup(c & 1, c >> 1);     // q4 = 0, 1, 2
                         else ppair(c - 6);                    // pairs of q4 = 0, 1
+                    } else if (NDC == 2) {                    // d = 32: two row groups per product
+                        pgroup(0, 2 * c);
+                        pgroup(1, 2 * c);
+                        ppair(2 * c);
+                        pgroup(0, 2 * c + 1);
+                        pgroup(1, 2 * c + 1);
+                        ppair(2 * c + 1);
                     } else if (c < 4) {                       // d = 64, 96
                         pgroup(0, c);
                         pgroup(1, c);
@@ -567,9 +574,14 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
                         if (ig(i) == c) dsitem(i);
                 }
                 // masks of the pending draw: block h after product c = 2h + 1
-                // (d >= 128) or h + 1 (d = 64)
-                if (DROPOUT && (NDC >= 8 ? (c & 1) && (c >> 1) < NBB : c >= 1 && c - 1 < NBB))
+                // (d >= 128), h + 1 (d = 64, 96), all after product 1 (d = 32)
+                if (DROPOUT && NDC == 2 && c == 1) {
+#pragma unroll
+                    for (int h = 0; h < NBB; ++h) mask_end_blk(pend, R + 1, h);
+                } else if (DROPOUT && NDC > 2 &&
+                           (NDC >= 8 ? (c & 1) && (c >> 1) < NBB : c >= 1 && c - 1 < NBB)) {
                     mask_end_blk(pend, R + 1, NDC >= 8 ? c >> 1 : c - 1);
+                }
                 if constexpr (NKP == 2) mma(dcur[1], of[c % 3], kv[1][c]);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -672,12 +684,14 @@ hipError_t launch_bwd_dkdv16(Elem e, int d, bool causal, bool dropout, const Bwd
                              hipStream_t stream) {
     switch (e) {
     case Elem::BF16:
-        return d == 64    ? launch_dkdv16_t<bf16, 64>(causal, dropout, a, stream)
+        return d == 32    ? launch_dkdv16_t<bf16, 32>(causal, dropout, a, stream)
+               : d == 64  ? launch_dkdv16_t<bf16, 64>(causal, dropout, a, stream)
                : d == 96  ? launch_dkdv16_t<bf16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_dkdv16_t<bf16, 128>(causal, dropout, a, stream)
                           : launch_dkdv16_t<bf16, 256>(causal, dropout, a, stream);
     case Elem::F16:
-        return d == 64    ? launch_dkdv16_t<f16, 64>(causal, dropout, a, stream)
+        return d == 32    ? launch_dkdv16_t<f16, 32>(causal, dropout, a, stream)
+               : d == 64  ? launch_dkdv16_t<f16, 64>(causal, dropout, a, stream)
                : d == 96  ? launch_dkdv16_t<f16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_dkdv16_t<f16, 128>(causal, dropout, a, stream)
                           : launch_dkdv16_t<f16, 256>(causal, dropout, a, stream);

@@ -324,20 +324,17 @@ hipError_t launch_fwd_merge(Elem e, int d, const FwdArgs &a, hipStream_t stream)
 
 hipError_t launch_fwd(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                       hipStream_t stream) {
-    // 16-bit inputs at d = 64, 96, 128 and 256 take the kernel of
-    // fa_fwd_pp.hip; every other case the generic one (32 rows per
-    // wavefront).
+    // 16-bit inputs take the kernel of fa_fwd_pp.hip; fp32 inputs the generic
+    // one (32 rows per wavefront).
     switch (e) {
     case Elem::BF16:
         switch (d) {
-        case 32: return launch_fwd_t<bf16, 32>(causal, dropout, a, stream);
-        case 64: case 96: case 128: case 256: return launch_fwd_pp(e, d, causal, dropout, a, stream);
+        case 32: case 64: case 96: case 128: case 256: return launch_fwd_pp(e, d, causal, dropout, a, stream);
         }
         break;
     case Elem::F16:
         switch (d) {
-        case 32: return launch_fwd_t<f16, 32>(causal, dropout, a, stream);
-        case 64: case 96: case 128: case 256: return launch_fwd_pp(e, d, causal, dropout, a, stream);
+        case 32: case 64: case 96: case 128: case 256: return launch_fwd_pp(e, d, causal, dropout, a, stream);
         }
         break;
     case Elem::F32:

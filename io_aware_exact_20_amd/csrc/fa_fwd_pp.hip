@@ -1,5 +1,5 @@
-// Forward of fused exact attention for 16-bit inputs at d = 64, 96, 128 and
-// 256 on gfx950, with two wavefronts per SIMD (one at d = 256).
+// Forward of fused exact attention for 16-bit inputs at d = 32, 64, 96, 128
+// and 256 on gfx950, with two wavefronts per SIMD (one at d = 256).
 //
 // The method is the one of the other forward kernels: Q, K, V tiled into
 // on-chip blocks, the online-softmax recurrence (running row maximum,
@@ -55,9 +55,9 @@ struct FwdPPTile {
     // 32-key blocks per tile: two without dropout (one barrier per 64 keys);
     // one with it (two measured no faster there and need the vector phase
     // inlined by force to stay out of scratch memory).
-    // (d = 96: always two, a 32-key tile being six load instructions for
-    // four wavefronts)
-    static constexpr int NKB = D == 96 ? 2 : (DROPOUT || D == 256) ? 1 : 2;
+    // (d = 96 and 32: always two, a 32-key tile being six or two load
+    // instructions for four wavefronts)
+    static constexpr int NKB = (D == 96 || D == 32) ? 2 : (DROPOUT || D == 256) ? 1 : 2;
     // K and V buffers each (two workgroups share the LDS); tiles are loaded
     // one step ahead.
     static constexpr int NBUF = 2;
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     constexpr int NDC = D / 16;       // contraction chunks of S
     constexpr int NDB = D / 32;       // 32-column blocks of O
     constexpr float kNegInf = -__builtin_huge_valf();
-    static_assert(D == 64 || D == 96 || D == 128 || D == 256, "tile plan for d = 64, 96, 128 and 256");
+    static_assert(D == 32 || D == 64 || D == 96 || D == 128 || D == 256, "tile plan for d = 32 ... 256");
     static_assert(2 * NDB == NDC, "one V^T product per K product");
 
     // LDS: K tile t in buffer t % 2, V tile t in buffer t % 2.
@@ -491,14 +491,16 @@ static hipError_t launch_fwd_pp_t(bool causal, bool dropout, const FwdArgs &a, h
 
 hipError_t launch_fwd_pp(Elem e, int d, bool causal, bool dropout, const FwdArgs &a,
                          hipStream_t stream) {
-    if (d != 64 && d != 96 && d != 128 && d != 256) return hipErrorInvalidValue;
+    if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return hipErrorInvalidValue;
     if (e == Elem::BF16)
-        return d == 64    ? launch_fwd_pp_t<bf16, 64>(causal, dropout, a, stream)
+        return d == 32    ? launch_fwd_pp_t<bf16, 32>(causal, dropout, a, stream)
+               : d == 64  ? launch_fwd_pp_t<bf16, 64>(causal, dropout, a, stream)
                : d == 96  ? launch_fwd_pp_t<bf16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_fwd_pp_t<bf16, 128>(causal, dropout, a, stream)
                           : launch_fwd_pp_t<bf16, 256>(causal, dropout, a, stream);
     if (e == Elem::F16)
-        return d == 64    ? launch_fwd_pp_t<f16, 64>(causal, dropout, a, stream)
+        return d == 32    ? launch_fwd_pp_t<f16, 32>(causal, dropout, a, stream)
+               : d == 64  ? launch_fwd_pp_t<f16, 64>(causal, dropout, a, stream)
                : d == 96  ? launch_fwd_pp_t<f16, 96>(causal, dropout, a, stream)
                : d == 128 ? launch_fwd_pp_t<f16, 128>(causal, dropout, a, stream)
                           : launch_fwd_pp_t<f16, 256>(causal, dropout, a, stream);

@@ -323,13 +323,13 @@ def test_full_size_fwd_bwd_every_head(gpu_lib, name):
 
 LONG_HD = [Workload("long_d%d_%s" % (d, dt), 1, 8, 4096, d, dt, causal=True, dropout_p=0.1,
                     backward=True, seed=5 + d, dropout_seed=workloads.DROPOUT_SEED)
-           for d in (96, 256) for dt in ("bf16", "f16")]
+           for d in (32, 96, 256) for dt in ("bf16", "f16")]
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("w", LONG_HD, ids=[w.name for w in LONG_HD])
 def test_full_length_other_head_dims(gpu_lib, w):
-    """d = 96 and 256 at the training sequence length (1 x 8 x 4096, causal,
+    """d = 32, 96 and 256 at the training sequence length (1 x 8 x 4096, causal,
     dropout 0.1; the layouts of those head dimensions: 64-key forward steps
     with dropout at d = 96, one workgroup per CU at d = 256, 64-key dK/dV and
     32-row dQ blocks at d = 256): every element of O, LSE, dQ, dK, dV."""
