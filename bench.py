@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, causal, d=128) + % of MFMA peak"
 # Sources of the 16-bit kernels each stage runs (the counters in
 # profiles/traffic.json are only used while these are unchanged).
-KERNEL_SOURCES = {"fwd": "fa_fwd_pp.hip", "bwd_dkdv": "fa_dkdv16.hip", "bwd_dq": "fa_bwd16.hip"}
+KERNEL_SOURCES = {"fwd": "fa_fwd_pp.hip", "bwd_dkdv": "fa_dkdv16.hip", "bwd_dq": "fa_dq16.hpp"}
 COPY_BYTES = 1 << 30             # the plain copy used to calibrate the HBM byte counters
 
 
