@@ -175,6 +175,9 @@ CROSS = [
     # d = 128 with fewer keys than queries: whole wavefronts of rows see no key
     ("bf16", 128, 1000, 300, True, 0.1), ("bf16", 128, 700, 250, True, 0.0),
     ("f16", 128, 600, 100, True, 0.1),
+    # the other head dimensions with queries and keys of two lengths
+    ("bf16", 32, 300, 700, True, 0.1), ("f16", 32, 500, 200, True, 0.0),
+    ("f16", 96, 400, 150, True, 0.1), ("bf16", 256, 130, 500, False, 0.1),
 ]
 
 
@@ -228,7 +231,8 @@ SPLITS = [
     ("bf16", 128, 300, 1000, False, 0.1, 3), ("bf16", 64, 256, 2048, True, 0.0, 7),
     ("bf16", 64, 1000, 300, True, 0.1, 2), ("f16", 128, 5, 3000, False, 0.0, 256),
     ("bf16", 256, 17, 1500, True, 0.1, 5), ("f32", 64, 9, 1000, True, 0.1, 4),
-    ("bf16", 128, 1024, 1024, True, 0.1, 4),
+    ("bf16", 128, 1024, 1024, True, 0.1, 4), ("bf16", 32, 40, 2000, True, 0.1, 6),
+    ("f16", 96, 130, 1100, False, 0.0, 3),
 ]
 
 
