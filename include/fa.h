@@ -65,9 +65,8 @@ typedef enum fa_dtype {
  *                (a zero extent is an empty problem: FA_OK, nothing
  *                launched); N < 2^31; d in {32, 64, 96, 128} for every
  *                dtype and also 256 for FA_BF16 / FA_F16 (other values:
- *                FA_EUNSUPPORTED).  d = 64 and 128 with 16-bit inputs run
- *                the tuned kernels; the other head dimensions (and fp32) run
- *                the generic ones.
+ *                FA_EUNSUPPORTED).  16-bit inputs run the tuned kernels at
+ *                every head dimension; fp32 inputs run the generic ones.
  *   dtype      : fa_dtype_t of q, k, v (and dout in the backward).
  *   causal     : 0 or 1.  With 1, key j is masked for query i when j > i
  *                (the diagonal is kept); masked probabilities are exactly 0.
