@@ -223,24 +223,59 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     f32x16 s[NKB];           // scores of the tile the vector phase works on next
     uint32_t pp[8 * NKB];    // rounded (kept) probabilities of the tile the matrix phase multiplies
 
+    // Keep-bit draw of a tile (two Philox blocks per 32-key block, see
+    // keep_masks_from_blocks).  With eight or more product pairs per matrix
+    // phase (d >= 96) it is staged: counters, then the block-rounds spread
+    // over the products of the matrix phase before the tile's vector phase
+    // (where a wavefront's own products hide a few vector instructions
+    // each), then the masks in the vector phase (d = 256 3 %, non-causal
+    // d = 128 3.5 % faster; neutral on causal d = 128).  With four (d = 32,
+    // 64) the rounds would crowd the products (measured 3 % slower), and the
+    // whole draw stays in the vector phase.
+    constexpr int NB2 = 2 * NKB, KU = 10 * NB2;   // blocks; block-rounds
+    constexpr bool STAGED = DROPOUT && NKB * NDC >= 8;
+    Philox4 kd[NB2];
+    auto keep_begin = [&](int t) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const uint32_t grp = (uint32_t)((klo + t * BC + 32 * kb) >> 3) + 2 * (uint32_t)g;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                kd[2 * kb + h].x[0] = grp + h;
+                kd[2 * kb + h].x[1] = (uint32_t)qrow;
+                kd[2 * kb + h].x[2] = h_idx;
+                kd[2 * kb + h].x[3] = b_idx;
+            }
+        }
+    };
+    // block-rounds u0 .. u1-1: unit u is round u / NB2 of block u % NB2
+    auto keep_rounds = [&](int u0, int u1) {
+#pragma unroll
+        for (int u = u0; u < u1; ++u) philox_round(kd[u % NB2], u / NB2, a.seed_lo, a.seed_hi);
+        if (u1 > u0) {
+#pragma unroll
+            for (int h = 0; h < NB2; ++h)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pin_vgpr(kd[h].x[q]);
+        }
+    };
+
     // Vector phase for tile t: scores s -> probabilities pp.
     auto vec_phase = [&](int t) __attribute__((always_inline)) {
         if (is_edge(t)) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) apply_mask(s[kb], t, kb);
         }
-        // Keep masks of each 32-key block's probability pairs (drawn before
-        // the scores are read into vector registers).
+        // Keep masks of each 32-key block's probability pairs, from the
+        // finished draw of tile t.
         uint32_t keep_m[NKB][8];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            if (DROPOUT) {
-                const uint32_t grp = (uint32_t)((klo + t * BC + 32 * kb) >> 3) + 2 * (uint32_t)g;
-                const Philox4 b0 = philox4x32_10(grp, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
-                const Philox4 b1 = philox4x32_10(grp + 1, (uint32_t)qrow, h_idx, b_idx, a.seed_lo, a.seed_hi);
-                keep_masks_from_blocks(b0, b1, kc2, keep_m[kb]);
-            }
+        if (DROPOUT && !STAGED) {
+            keep_begin(t);
+            keep_rounds(0, KU);
         }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            if (DROPOUT) keep_masks_from_blocks(kd[2 * kb], kd[2 * kb + 1], kc2, keep_m[kb]);
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -288,7 +323,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     // scores of the tile after it, which are never used: every phase has one
     // shape.  The S chain and the O products alternate, so no product waits
     // for the one just issued; fragments are read two product pairs ahead.
-    auto mat_phase = [&](auto m_c) {
+    auto mat_phase = [&](auto m_c, int t) {
         constexpr int M = decltype(m_c)::value;
         constexpr int NJ = NKB * NDC;   // products of each kind (S: key block x d chunk; O: key chunk x d block)
         constexpr int MK = (M + 1) % NBUF;
@@ -314,6 +349,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+        if (STAGED) keep_begin(t + 1);
         frag_t<T> kf[3], vf[3];
         kf[0] = kfrag(0);
         vf[0] = vfrag(0);
@@ -326,6 +362,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
                 vf[(j + 2) % 3] = vfrag(j + 2);
             }
             mma(s[j / NDC], kf[j % 3], qf[j % NDC]);
+            if (STAGED) keep_rounds((KU * j) / NJ, (KU * (j + 1)) / NJ);
             mma(o[j % NDB], vf[j % 3], pfrag(j / NDB));
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -370,6 +407,10 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     }
     __syncthreads();   // K buffer 0 is refilled before step 0
     load_kv(2, 0, 1, 1);   // K_2, V_1
+    if (STAGED) {          // keep bits of tile 0
+        keep_begin(0);
+        keep_rounds(0, KU);
+    }
 
     // ---- steps.  Every wavefront runs the phase sequence vec(0) mat(0)
     // vec(1) mat(1) ... mat(Tw-1), with the barrier of step t-1 between
@@ -384,7 +425,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
         constexpr int M = decltype(m_c)::value;
         vec_phase(t);
         if (t > 0) end_step(std::integral_constant<int, (M + 1) % 2>{}, t - 1);
-        mat_phase(m_c);
+        mat_phase(m_c, t);
     };
     auto end_step_rt = [&](int t) {   // run-time t % 2 (no LDS reads follow)
         if (t % 2 == 0) end_step(I0{}, t);
