@@ -21,7 +21,11 @@
 // A workgroup has four wavefronts (128 rows) and two workgroups share a CU,
 // so the two wavefronts of a SIMD come from different workgroups and one
 // runs while the other waits at its step barrier.  Steps cover 64 keys
-// without dropout and 32 keys with it.
+// without dropout and 32 keys with it (d = 32 and 96: 64 keys also with
+// dropout).  The translation unit is compiled with matrix-core results in
+// VGPRs: Q, the output accumulator and the scores all sit in VGPRs (at
+// d = 128 202-213 of a wavefront's 256), so the vector phase reads the
+// scores without a copy out of AGPRs.
 //
 // At d = 256 the output accumulator (128 registers) and Q (64) leave no room
 // for a second wavefront per SIMD: one workgroup per CU, one wavefront per
@@ -286,17 +290,8 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
             const float m_new = fmaxf(m_run, max_halves(mx) * sl2);
             const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
             l_run *= alpha;
-            // One block at a time, back into the accumulation registers
-            // (the accumulators live there; a whole-tile multiply would pull
-            // all of them into vector registers).
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                f32x16 x = o[db];
-                pin_vgpr(x);   // explicit copy out of the accumulation registers
-                x *= alpha;
-                pin_agpr(x);   // and back
-                o[db] = x;
-            }
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
             m_run = m_new;
         }
         const float mu = m_run == kNegInf ? 0.f : m_run;
@@ -393,8 +388,6 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     // 0 (K_2, V_1).
     load_kv(0, 0, 0, 0);
     load_kv(1, 1, 0, 0);   // (V_0 loaded twice: same data, same place)
-#pragma unroll
-    for (int c = 0; c < NDC; ++c) pin_agpr(qf[c]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (Tw > 0) {
