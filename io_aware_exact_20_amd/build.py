@@ -27,15 +27,15 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 
 # Kernel sources: the inputs are finite by contract (infinities are still
 # honoured, they carry the masks), so NaN-preserving canonicalisation of
-# max() is not needed.  The forward kernels, the dK/dV kernel and the dQ
-# kernel at d = 32 to 128 select matrix-core results into VGPRs, so that
-# the softmax and dS arithmetic reads them without AGPR copies; the FP8
-# forward and the d = 256 dQ kernel leave them in AGPRs, which hold their
-# output accumulators.
+# max() is not needed.  The forward kernels (16-bit and FP8), the dK/dV
+# kernel and the dQ kernel at d = 32 to 128 select matrix-core results into
+# VGPRs, so that the softmax and dS arithmetic reads them without AGPR
+# copies; the d = 256 dQ kernel leaves them in AGPRs, which hold its output
+# accumulators.
 KERNEL_FLAGS = ["-fno-honor-nans"]
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 PER_SOURCE = {"fa_fwd.hip": KERNEL_FLAGS + VGPR_FORM, "fa_fwd_pp.hip": KERNEL_FLAGS + VGPR_FORM,
-              "fa_fwd_fp8.hip": KERNEL_FLAGS, "fa_bwd16.hip": KERNEL_FLAGS + VGPR_FORM,
+              "fa_fwd_fp8.hip": KERNEL_FLAGS + VGPR_FORM, "fa_bwd16.hip": KERNEL_FLAGS + VGPR_FORM,
               "fa_dq256.hip": KERNEL_FLAGS,
               "fa_dkdv16.hip": KERNEL_FLAGS + VGPR_FORM}
 

@@ -226,13 +226,7 @@ __global__ void __launch_bounds__(kF8Threads, kF8WgPerCu) fwd_fp8_kernel(const F
             const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                f32x16 x = o[db];
-                pin_vgpr(x);
-                x *= alpha;
-                pin_agpr(x);
-                o[db] = x;
-            }
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
             m_run = m_new;
         }
         const float mu = (m_run == kNegInf ? 0.f : m_run) - kF8PScaleLog2;
@@ -317,8 +311,6 @@ __global__ void __launch_bounds__(kF8Threads, kF8WgPerCu) fwd_fp8_kernel(const F
     };
     load_kv(0, 0, 0, 0);
     load_kv(1, 1, 0, 0);
-    pin_agpr(qf[0]);
-    pin_agpr(qf[1]);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (Tw > 0) {
