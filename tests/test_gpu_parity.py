@@ -138,8 +138,9 @@ for dt, dims in (("bf16", (32, 96, 256)), ("f16", (32, 96, 256)), ("f32", (32, 9
 
 @pytest.mark.parametrize("w", HEAD_DIMS, ids=[w.name for w in HEAD_DIMS])
 def test_other_head_dims_fwd_bwd_full(gpu_lib, w):
-    """Head dimensions 32, 96 and 256 (generic kernels): every element of O,
-    LSE, dQ, dK, dV at N=300, masks, dropout, all input types (256: 16-bit)."""
+    """Head dimensions 32, 96 and 256 (16-bit inputs: the tuned kernels; fp32:
+    the generic ones): every element of O, LSE, dQ, dK, dV at N=300, masks,
+    dropout, all input types (256: 16-bit)."""
     log("case %s" % w.name)
     q, k, v, do = workloads.draw(w)
     edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
@@ -587,16 +588,25 @@ def test_empty_problem(gpu_lib):
     assert dq.shape == q.shape
 
 
-def test_out_f32_matches_oracle(gpu_lib):
-    w = Workload("outf32", 1, 2, 200, 128, "bf16", causal=True, dropout_p=0.1, backward=True,
-                 seed=21, dropout_seed=4)
+# fp32 outputs from the 16-bit kernels: every head dimension (each has its
+# own epilogue instantiation; d = 256 dQ its own translation unit).
+OUT_F32 = [(32, "bf16", True, 0.1), (64, "f16", True, 0.1), (96, "bf16", True, 0.1),
+           (128, "bf16", True, 0.1), (256, "f16", True, 0.1), (256, "bf16", False, 0.0)]
+
+
+@pytest.mark.parametrize("d,dt,causal,p", OUT_F32,
+                         ids=["d%d_%s_c%d_p%g" % c for c in OUT_F32])
+def test_out_f32_matches_oracle(gpu_lib, d, dt, causal, p):
+    w = Workload("outf32", 1, 2, 200, d, dt, causal=causal, dropout_p=p, backward=True,
+                 seed=21 + d, dropout_seed=4)
     q, k, v, do = workloads.draw(w)
     o, lse, dq, dk, dv = run_bwd(gpu_lib, w, q, k, v, do, out_f32=True)
     assert o.dtype == torch.float32 and dq.dtype == torch.float32
+    assert dk.dtype == torch.float32 and dv.dtype == torch.float32
     edq, edk, edv, eo, elx = oracle_bwd(w, q, k, v, do)
     for name, got, exact in (("O", o, eo), ("LSE", lse, elx), ("dQ", dq, edq),
                              ("dK", dk, edk), ("dV", dv, edv)):
-        compare(name, got, exact, "bf16")
+        compare(name, got, exact, dt)
 
 
 def test_forward_is_deterministic(gpu_lib):
