@@ -276,7 +276,7 @@ def config_table(fa, dev, budget_s=2.0):
             frac = keys.sum() / (w.N * (w.N + 1) / 2 if w.causal else w.N * w.N)
             row["oracle"] = {"seconds": round(t, 2), "cores": oracle.num_threads(),
                              "sample": "%d rows of head (0,0)" % len(rws),
-                             "whole_workload_s_extrapolated": round(t / frac * w.B * w.H, 1)}
+                             "whole_workload_s_extrapolated": round(float(t / frac) * w.B * w.H, 1)}
             row["errors_on_sample"] = {nm: dict(zip(("max_abs", "mean_abs"),
                                                     [float("%.3e" % x) for x in _err(g[0, 0, rws], e)]))
                                        for nm, g, e in (("O", prob.o, eo), ("LSE", prob.lse, el))}
