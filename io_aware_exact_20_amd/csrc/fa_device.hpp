@@ -87,10 +87,11 @@ __device__ __forceinline__ frag_t<T> pack8(const f32x16 &x, int off) {
 
 // ------------------------------------------------------------ lane exchange
 //
-// Exchanges between the two halves of a wavefront (lane ^ 32) go through
-// ds_bpermute.  (v_permlane32_swap would avoid the LDS crossbar, but when fed
-// the same value for both operands this compiler treats its two results as
-// equal and drops the partner's value, so it is not used.)
+// Exchanges of one value between the two halves of a wavefront (lane ^ 32)
+// go through ds_bpermute: v_permlane32_swap fed the same value as both
+// operands has its two results treated as equal by this compiler, which then
+// drops the partner's value.  Where two different values are traded (the
+// keep-mask words, keep_masks_from_blocks) the swap is used.
 
 __device__ __forceinline__ uint32_t lane_in_wave() { return threadIdx.x & (kWave - 1); }
 
@@ -228,15 +229,6 @@ __device__ __forceinline__ frag_t<T> load_frag(const T *p) {
         t.a = reinterpret_cast<const uint4 *>(p)[0];
         t.b = reinterpret_cast<const uint4 *>(p)[1];
         return __builtin_bit_cast(frag_t<T>, t);
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ half_t<T> load_half(const T *p) {
-    if constexpr (sizeof(T) == 2) {
-        return __builtin_bit_cast(half_t<T>, *reinterpret_cast<const uint2 *>(p));
-    } else {
-        return __builtin_bit_cast(half_t<T>, *reinterpret_cast<const uint4 *>(p));
     }
 }
 
@@ -389,12 +381,6 @@ __device__ __forceinline__ half_t<T> lds_half_tr(const lds_char *p) {
     return __builtin_bit_cast(half_t<T>, r);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's data
-// lands at base + 16 l (base must be uniform across the wavefront).
-__device__ __forceinline__ void g2lds16(const void *gptr, lds_char *base) {
-    __builtin_amdgcn_global_load_lds(gptr, (FA_LDS void *)base, 16, 0, 0);
-}
-
 // Buffer resource over `bytes` bytes from `p` (raw, unswizzled).  Loads
 // through it whose 16 bytes lie past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
@@ -476,7 +462,5 @@ __device__ __forceinline__ float sum2_dot<f16>(uint32_t pair, float acc) {
 // --------------------------------------------------------------- utilities
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <typename T> __device__ __forceinline__ T zero_el() { return from_f32<T>(0.f); }
 
 }  // namespace fa
