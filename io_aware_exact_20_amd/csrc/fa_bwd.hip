@@ -96,9 +96,12 @@ __global__ void __launch_bounds__(256) bwd_pre_kernel(const BwdArgs a, int64_t r
 
 // ---------------------------------------------------------------- dK, dV
 
+// The generic dK/dV and dQ kernels serve fp32 inputs (16-bit inputs take
+// fa_dkdv16.hip and fa_dq16.hpp).
 template <typename T, int D>
 struct DkdvTile {
-    static constexpr int NW = sizeof(T) == 4 ? 2 : 4;   // wavefronts per workgroup
+    static_assert(sizeof(T) == 4, "generic dK/dV: fp32 inputs");
+    static constexpr int NW = 2;                        // wavefronts per workgroup
     static constexpr int THREADS = NW * kWave;
     static constexpr int BK = 32 * NW;                  // keys per workgroup
     static constexpr int BQ = 32;                       // query rows per tile
@@ -296,13 +299,14 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(const BwdArgs a) {
 
 template <typename T, int D>
 struct DqTile {
+    static_assert(sizeof(T) == 4, "generic dQ: fp32 inputs");
     static constexpr int NW = 4;
     static constexpr int THREADS = NW * kWave;
     static constexpr int BQ = 32 * NW;           // query rows per workgroup
     static constexpr int BC = 64;                // keys per LDS tile
     static constexpr int CH = 16 / sizeof(T);
     static constexpr int LD = D + CH;
-    static constexpr int MIN_WG_PER_CU = (sizeof(T) == 4 || D > 128) ? 1 : 2;
+    static constexpr int MIN_WG_PER_CU = 1;
 };
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>

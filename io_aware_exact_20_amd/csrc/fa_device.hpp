@@ -251,37 +251,24 @@ __device__ __forceinline__ void store4(T *p, float a, float b, float c, float d)
 
 // ---------------------------------------------------------- transposed reads
 //
-// Half-fragment of a transposed operand read from a row-major LDS tile:
-// lane l (i = l % 32, g = l / 32) receives tile[rbase + 4g + k][c0 + i] for
-// k = 0..3.  Two such reads (rbase and rbase + 8) give the eight slots of a
-// fragment whose contraction index runs along the tile's rows in the order
-// rbase + 4g + {0..3}, rbase + 8 + 4g + {0..3} -- the order in which a
-// 32x32 accumulator holds the same rows (register r -> row 8(r/4) + 4g +
-// r%4), so a rounded accumulator is the matching other operand.
-//
-// For 16-bit types this is one ds_read_b64_tr_b16: within each group of 16
-// lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
-// 4k + i/4 (k = 0..3), so lane 4k + j of group G addresses row
-// rbase + 4(G/2) + k at column c0 + 16(G%2) + 4j.  fp32 tiles are read
-// element by element.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
+// Half-fragment of a transposed fp32 operand read from a row-major LDS tile
+// (the generic fp32 kernels): lane l (i = l % 32, g = l / 32) receives
+// tile[rbase + 4g + k][c0 + i] for k = 0..3.  Two such reads (rbase and
+// rbase + 8) give the eight slots of a fragment whose contraction index runs
+// along the tile's rows in the order rbase + 4g + {0..3}, rbase + 8 + 4g +
+// {0..3} -- the order in which a 32x32 accumulator holds the same rows
+// (register r -> row 8(r/4) + 4g + r%4), so a rounded accumulator is the
+// matching other operand.  (The 16-bit kernels read their swizzled tiles
+// with ds_read_b64_tr_b16 through lds_half_tr.)
 template <typename T>
 __device__ __forceinline__ half_t<T> load_half_tr(const T *tile, int ld, int rbase, int c0) {
+    static_assert(sizeof(T) == 4, "element-wise transposed reads serve fp32 tiles");
     const int lane = (int)lane_in_wave();
-    if constexpr (sizeof(T) == 2) {
-        const int G = lane >> 4, k = (lane >> 2) & 3, j = lane & 3;
-        const T *p = tile + (rbase + 4 * (G >> 1) + k) * ld + c0 + 16 * (G & 1) + 4 * j;
-        const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(p));
-        return __builtin_bit_cast(half_t<T>, r);
-    } else {
-        const int i = lane & 31, g = lane >> 5;
-        half_t<T> h;
+    const int i = lane & 31, g = lane >> 5;
+    half_t<T> h;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) h[k] = tile[(rbase + 4 * g + k) * ld + c0 + i];
-        return h;
-    }
+    for (int k = 0; k < 4; ++k) h[k] = tile[(rbase + 4 * g + k) * ld + c0 + i];
+    return h;
 }
 
 template <typename T>
@@ -374,7 +361,10 @@ __device__ __forceinline__ frag_t<T> lds_frag(const lds_char *p) {
     return __builtin_bit_cast(frag_t<T>, *(const FA_LDS u32x4 *)p);
 }
 
-// Transposed half-fragment read (ds_read_b64_tr_b16).
+// Transposed half-fragment read (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
+// 4k + i/4 (k = 0..3).
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <typename T>
 __device__ __forceinline__ half_t<T> lds_half_tr(const lds_char *p) {
     const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4 *)p);

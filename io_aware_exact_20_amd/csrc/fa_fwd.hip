@@ -30,15 +30,17 @@
 
 namespace fa {
 
+// The generic forward serves fp32 inputs (16-bit inputs take fa_fwd_pp.hip).
 template <typename T, int D>
 struct FwdTile {
+    static_assert(sizeof(T) == 4, "generic forward: fp32 inputs");
     static constexpr int NW = 4;                  // wavefronts per workgroup
     static constexpr int THREADS = NW * kWave;
     static constexpr int BQ = 32 * NW;            // query rows per workgroup
     static constexpr int BC = 64;                 // keys per LDS tile
     static constexpr int CH = 16 / sizeof(T);     // elements per 16-byte access
     static constexpr int LD = D + CH;             // K and V row pitch in LDS (elements)
-    static constexpr int MIN_WG_PER_CU = (sizeof(T) == 4 || D > 128) ? 1 : 2;
+    static constexpr int MIN_WG_PER_CU = 1;
 };
 
 template <typename T, int D, bool CAUSAL, bool DROPOUT>
