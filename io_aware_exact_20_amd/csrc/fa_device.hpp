@@ -119,17 +119,26 @@ struct Philox4 { uint32_t x[4]; };
 constexpr uint32_t kPhiloxWeylA = 0x9E3779B9u, kPhiloxWeylB = 0xBB67AE85u;
 
 // Round r (0-based) of the generator on counter c under key (k0, k1): the
-// round key is the key advanced r times by the Weyl increments.
+// round key is the key advanced r times by the Weyl increments.  With
+// FLIP, the last round (r = 9) also flips the top bit of both 16-bit halves
+// of output words 0 and 2, through its round key (a uniform value, so the
+// flip costs no vector instruction); keep_masks_from_blocks and
+// keep_mask2_flipped expect words drawn this way.  The forward and the dQ
+// kernel draw with the flip (1.2 % and 0.6 % faster); in the dK/dV kernel
+// it changed the register allocation for the worse (3 % slower at d = 128),
+// so that kernel draws plain words and compares them with keep_mask2.
+template <bool FLIP = false>
 __device__ __forceinline__ void philox_round(Philox4 &c, int r, uint32_t k0, uint32_t k1) {
     constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+    const uint32_t flip = (FLIP && r == 9) ? 0x80008000u : 0u;
     // One 32x32->64-bit product per word pair (v_mad_u64_u32 gives both
     // halves in a single instruction).
     const uint64_t pA = (uint64_t)kMulA * c.x[0], pB = (uint64_t)kMulB * c.x[2];
     const uint32_t hiA = (uint32_t)(pA >> 32), loA = (uint32_t)pA;
     const uint32_t hiB = (uint32_t)(pB >> 32), loB = (uint32_t)pB;
     // Three-input XORs as single v_bitop3_b32 instructions (truth table 0x96).
-    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hiB, c.x[1], k0 + (uint32_t)r * kPhiloxWeylA, 0x96);
-    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hiA, c.x[3], k1 + (uint32_t)r * kPhiloxWeylB, 0x96);
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hiB, c.x[1], (k0 + (uint32_t)r * kPhiloxWeylA) ^ flip, 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hiA, c.x[3], (k1 + (uint32_t)r * kPhiloxWeylB) ^ flip, 0x96);
     c.x[0] = n0; c.x[1] = loB; c.x[2] = n2; c.x[3] = loA;
 }
 
@@ -163,18 +172,22 @@ __device__ __forceinline__ uint32_t keep_byte(uint32_t grp, uint32_t row, uint32
 // the signed one; then lane >= T exactly when the saturating 16-bit difference
 // (T' - 1) - lane' is negative (T', lane': flipped), and an arithmetic shift
 // spreads its sign over the half.  kc2 = keep_cmp_const(T), 1 <= T <= 65535.
+// keep_mask2_flipped takes a word whose halves are already flipped.
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 __host__ __device__ constexpr uint32_t keep_cmp_const(uint32_t T) {
     return (((T ^ 0x8000u) - 1u) & 0xFFFFu) * 0x00010001u;
 }
-__device__ __forceinline__ uint32_t keep_mask2(uint32_t w, uint32_t kc2) {
-    const i16x2 lane = __builtin_bit_cast(i16x2, w ^ 0x80008000u);
-    const i16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(i16x2, kc2), lane);
+__device__ __forceinline__ uint32_t keep_mask2_flipped(uint32_t wf, uint32_t kc2) {
+    const i16x2 d = __builtin_elementwise_sub_sat(__builtin_bit_cast(i16x2, kc2), __builtin_bit_cast(i16x2, wf));
     return __builtin_bit_cast(uint32_t, d >> (i16x2){15, 15});
+}
+__device__ __forceinline__ uint32_t keep_mask2(uint32_t w, uint32_t kc2) {
+    return keep_mask2_flipped(w ^ 0x80008000u, kc2);
 }
 
 // Keep masks (keep_mask2 layout) of the eight probability pairs one lane
-// holds in a 32x32 accumulator with one query row per lane: pair i is
+// holds in a 32x32 accumulator with one query row per lane, from blocks
+// drawn with philox_round<true> (words 0 and 2 flipped): pair i is
 // registers 2i, 2i+1, keys 8(i/2) + 4g + 2(i%2) + {0, 1} of the 32-key block
 // (g = lane / 32).  Lane (row, g) draws 8-key blocks 2g (b0) and 2g+1 (b1)
 // of the row; pair i takes word 2g + i%2 of block i/2.  So the lower half
@@ -189,9 +202,10 @@ __device__ __forceinline__ void keep_masks_from_blocks(const Philox4 &b0, const 
         const Philox4 &b = h ? b1 : b0;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
+            // e = 0 trades words 0 and 2 (drawn flipped), e = 1 words 1 and 3
             const auto r = __builtin_amdgcn_permlane32_swap(b.x[e], b.x[2 + e], false, false);
-            m[2 * h + e] = keep_mask2(r[0], kc2);       // block h: pairs 2h + e
-            m[4 + 2 * h + e] = keep_mask2(r[1], kc2);   // block 2 + h: pairs 4 + 2h + e
+            m[2 * h + e] = e ? keep_mask2(r[0], kc2) : keep_mask2_flipped(r[0], kc2);         // block h: pairs 2h + e
+            m[4 + 2 * h + e] = e ? keep_mask2(r[1], kc2) : keep_mask2_flipped(r[1], kc2);     // block 2 + h: pairs 4 + 2h + e
         }
     }
 }

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
     };
     auto keep_rounds = [&](KeepDraw &k, int u0, int u1) {
 #pragma unroll
-        for (int u = u0; u < u1; ++u) philox_round(k.c[u & 1], u >> 1, a.seed_lo, a.seed_hi);
+        for (int u = u0; u < u1; ++u) philox_round<true>(k.c[u & 1], u >> 1, a.seed_lo, a.seed_hi);
         if (u1 > u0) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)

@@ -255,7 +255,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
     // block-rounds u0 .. u1-1: unit u is round u / NB2 of block u % NB2
     auto keep_rounds = [&](int u0, int u1) {
 #pragma unroll
-        for (int u = u0; u < u1; ++u) philox_round(kd[u % NB2], u / NB2, a.seed_lo, a.seed_hi);
+        for (int u = u0; u < u1; ++u) philox_round<true>(kd[u % NB2], u / NB2, a.seed_lo, a.seed_hi);
         if (u1 > u0) {
 #pragma unroll
             for (int h = 0; h < NB2; ++h)
