@@ -125,8 +125,8 @@ constexpr uint32_t kPhiloxWeylA = 0x9E3779B9u, kPhiloxWeylB = 0xBB67AE85u;
 // flip costs no vector instruction); keep_masks_from_blocks and
 // keep_mask2_flipped expect words drawn this way.  The forward and the dQ
 // kernel draw with the flip (1.2 % and 0.6 % faster); in the dK/dV kernel
-// it changed the register allocation for the worse (3 % slower at d = 128),
-// so that kernel draws plain words and compares them with keep_mask2.
+// only the B wavefronts do (with A's draws flipped too, its register
+// allocation came out 3 % slower at d = 128; B alone: 1-2 % faster).
 template <bool FLIP = false>
 __device__ __forceinline__ void philox_round(Philox4 &c, int r, uint32_t k0, uint32_t k1) {
     constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;

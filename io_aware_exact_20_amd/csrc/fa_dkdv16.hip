@@ -255,10 +255,14 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     // u % NB (NB = NBA or NBB, a compile-time constant at every call).  The
     // state is pinned afterwards so that the rounds stay in the group that
     // issues them.
+    struct CNB : std::integral_constant<int, NBB> {};   // a type of its own even when NBB == NBA
     auto mask_rounds = [&](auto nb_c, MaskDraw &m, int u0, int u1) {
         constexpr int NB = decltype(nb_c)::value;
+        // B's draws end with the folded flip of words 0 and 2 (its masks
+        // are formed with keep_mask2_flipped for them); A's are plain.
+        constexpr bool FLIP = std::is_same<decltype(nb_c), CNB>::value;
 #pragma unroll
-        for (int u = u0; u < u1; ++u) philox_round(m.c[u % NB], u / NB, a.seed_lo, a.seed_hi);
+        for (int u = u0; u < u1; ++u) philox_round<FLIP>(m.c[u % NB], u / NB, a.seed_lo, a.seed_hi);
         if (u1 > u0) {
 #pragma unroll
             for (int h = 0; h < NB; ++h)
@@ -273,7 +277,8 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
         FA_LDS char *p = (FA_LDS char *)mk[slot & (DROPOUT ? 3 : 0)][pair] + lq * MP + 16 * (jb0 + h);
         u32x4 w;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = keep_mask2(m.c[h].x[q], kc2);
+        for (int q = 0; q < 4; ++q)
+            w[q] = (role != 0 && !(q & 1)) ? keep_mask2_flipped(m.c[h].x[q], kc2) : keep_mask2(m.c[h].x[q], kc2);
         *(FA_LDS u32x4 *)p = w;
     };
     MaskDraw pend;   // draw whose masks are stored in the first phase of the next step
@@ -291,7 +296,6 @@ __global__ void __launch_bounds__(256, 1) dkdv16_kernel(const BwdArgs a) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using CNA = std::integral_constant<int, NBA>;
-    using CNB = std::integral_constant<int, NBB>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     using YES = std::true_type;
