@@ -179,6 +179,8 @@ CROSS = [
     # the other head dimensions with queries and keys of two lengths
     ("bf16", 32, 300, 700, True, 0.1), ("f16", 32, 500, 200, True, 0.0),
     ("f16", 96, 400, 150, True, 0.1), ("bf16", 256, 130, 500, False, 0.1),
+    # d = 256 causal with dropout (its dQ finishes each tile in one step)
+    ("f16", 256, 300, 700, True, 0.1), ("bf16", 256, 500, 130, True, 0.1),
 ]
 
 
@@ -204,6 +206,8 @@ CROSS_BWD = [
     ("f16", 128, 129, 64, True, 0.0), ("bf16", 96, 70, 250, True, 0.1),
     ("bf16", 256, 40, 100, True, 0.0), ("f32", 64, 77, 200, True, 0.1),
     ("f32", 128, 100, 33, False, 0.0),
+    # d = 256 causal with dropout (its dQ finishes each tile in one step)
+    ("f16", 256, 300, 700, True, 0.1), ("bf16", 256, 500, 130, True, 0.1),
 ]
 
 
