@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(kPPThreads, kPPWgPerCu<D>) fwd_pp_kernel(const
         if (u1 > u0) {
 #pragma unroll
             for (int h = 0; h < NB2; ++h)
-                // not after a block's round 0: two of its words are then
+                // not after a block's first generator round: two of its words are then
                 // loop-invariant, and a pin would copy them into every
                 // block's registers (0.5-1.3 % slower forward)
                 if ((u1 + NB2 - 1 - h) / NB2 >= 2)
