@@ -613,6 +613,30 @@ def test_out_f32_matches_oracle(gpu_lib, d, dt, causal, p):
         compare(name, got, exact, dt)
 
 
+def test_runs_on_the_callers_stream(gpu_lib):
+    """Work goes to the caller's current stream: inputs produced on a side
+    stream (default priority) right before the calls, forward and backward
+    enqueued on it, give bitwise the default-stream results (both passes
+    are deterministic)."""
+    w = Workload("stream", 2, 4, 640, 128, "bf16", causal=True, dropout_p=0.1, backward=True,
+                 seed=12, dropout_seed=0x5EED)
+    q, k, v, do = workloads.draw(w)
+    ref = run_bwd(gpu_lib, w, q, k, v, do)
+    qd, kd, vd, dod = (t.to("cuda") for t in (q, k, v, do))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        # the inputs are rewritten on the side stream just before the calls
+        q2, k2, v2, do2 = (t * 1.0 for t in (qd, kd, vd, dod))
+        o, lse = gpu_lib.fwd(q2, k2, v2, scale=w.softmax_scale, causal=w.causal,
+                             dropout_p=w.dropout_p, seed=w.dropout_seed)
+        dq, dk, dv = gpu_lib.bwd(q2, k2, v2, o, lse, do2, scale=w.softmax_scale, causal=w.causal,
+                                 dropout_p=w.dropout_p, seed=w.dropout_seed)
+    side.synchronize()
+    for name, got, want in zip(("O", "LSE", "dQ", "dK", "dV"), (o, lse, dq, dk, dv), ref):
+        assert torch.equal(got, want), name
+
+
 def test_forward_is_deterministic(gpu_lib):
     w = workloads.WORKLOADS["train_dropout"]
     w = Workload("det", 2, 4, 1024, 128, "bf16", causal=True, dropout_p=0.1, seed=3,
