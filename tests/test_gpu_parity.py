@@ -647,7 +647,7 @@ def test_forward_is_deterministic(gpu_lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 def test_backward_is_deterministic(gpu_lib, d):
     """No atomics anywhere: two backward runs on the same inputs agree bit for
     bit (a race between the wavefronts sharing LDS buffers would show here)."""
