@@ -240,8 +240,13 @@ __global__ void __launch_bounds__(256, 1) dq16_kernel(const BwdArgs a) {
         if (u1 > u0) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
+                // d <= 128: not after a block's first generator round (two
+                // of its words are then loop-invariant, and a pin would copy
+                // them; 0.4-1.6 % faster); the d = 256 kernel keeps every
+                // pin (1.2 % slower without)
+                if (NRB == 1 || (u1 + 1 - h) / 2 >= 2)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) pin_vgpr(k.c[h].x[q]);
+                    for (int q = 0; q < 4; ++q) pin_vgpr(k.c[h].x[q]);
         }
     };
     const uint32_t kc2 = keep_cmp_const(a.drop_T);
